@@ -1,0 +1,194 @@
+"""CPU oracle for MXFP8 (OCP-MX block-scaled FP8) quantize, dequantize and GEMM.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product library never does.  The
+arithmetic lives in ``mxo.c`` (plain C, built with gcc, FP64, table search for the
+FP8 encoding, literal search for the scale exponent); this module only marshals
+numpy arrays through ctypes.  ``oracle.exact`` is an independent exact-rational
+twin used to pin the C code on small inputs.
+
+Source: "Low-Precision GPU Programming" (leetllm.com) -- sections "Format taxonomy",
+"Numerical hazards", "Scale ownership and the GEMM dataflow", "Scaling architectures",
+"Microscaling: the two-row experiment".  See ``mxo.c`` for the per-function citations.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmxo.so")
+_SRC = os.path.join(_HERE, "mxo.c")
+
+FMT = {"e4m3": 0, "e5m2": 1}
+SRC = {"f32": 0, "bf16": 1}
+
+
+def build(force: bool = True) -> str:
+    """Compile mxo.c into libmxo.so with gcc (-O2, OpenMP, strict IEEE: no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        L = ctypes.CDLL(_LIB_PATH)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        i64 = ctypes.c_int64
+        vp = ctypes.c_void_p
+        L.mxo_decode.restype = ctypes.c_double
+        L.mxo_decode.argtypes = [ctypes.c_uint8, ctypes.c_int]
+        L.mxo_decode_e8m0.restype = ctypes.c_double
+        L.mxo_decode_e8m0.argtypes = [ctypes.c_uint8]
+        L.mxo_fmax.restype = ctypes.c_double
+        L.mxo_fmax.argtypes = [ctypes.c_int]
+        L.mxo_encode.restype = ctypes.c_uint8
+        L.mxo_encode.argtypes = [ctypes.c_double, ctypes.c_int]
+        L.mxo_scale_byte.restype = ctypes.c_int
+        L.mxo_scale_byte.argtypes = [ctypes.c_double, ctypes.c_int]
+        L.mxo_num_finite_codes.restype = ctypes.c_int
+        L.mxo_num_finite_codes.argtypes = [ctypes.c_int]
+        L.mxo_round_bf16.restype = ctypes.c_uint16
+        L.mxo_round_bf16.argtypes = [ctypes.c_double]
+        L.mxo_quantize.restype = None
+        L.mxo_quantize.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                   vp, i64, vp, i64]
+        L.mxo_dequantize.restype = None
+        L.mxo_dequantize.argtypes = [vp, i64, vp, i64, ctypes.c_int, i64, i64, vp, ctypes.c_int, i64]
+        L.mxo_gemm.restype = None
+        L.mxo_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, ctypes.c_int,
+                               vp, i64, vp, i64, ctypes.c_int, ctypes.c_double, vp, vp, vp]
+        L.mxo_gemm_sampled.restype = None
+        L.mxo_gemm_sampled.argtypes = [i64, vp, i64, vp, i64, ctypes.c_int,
+                                       vp, i64, vp, i64, ctypes.c_int, ctypes.c_double, vp,
+                                       i64, vp, vp, vp, vp]
+        _ = u8p
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ----------------------------------------------------------------- scalar codec
+
+def decode(code: int, fmt: str) -> float:
+    return lib().mxo_decode(code, FMT[fmt])
+
+
+def decode_e8m0(c: int) -> float:
+    return lib().mxo_decode_e8m0(c)
+
+
+def fmax(fmt: str) -> float:
+    return lib().mxo_fmax(FMT[fmt])
+
+
+def encode(a: float, fmt: str) -> int:
+    return int(lib().mxo_encode(float(a), FMT[fmt]))
+
+
+def scale_byte(amax: float, fmt: str) -> int:
+    return int(lib().mxo_scale_byte(float(amax), FMT[fmt]))
+
+
+def num_finite_codes(fmt: str) -> int:
+    return int(lib().mxo_num_finite_codes(FMT[fmt]))
+
+
+def round_bf16(v: float) -> int:
+    return int(lib().mxo_round_bf16(float(v)))
+
+
+# ----------------------------------------------------------------- array ops
+
+def _src_type(src: np.ndarray) -> int:
+    if src.dtype == np.float32:
+        return SRC["f32"]
+    if src.dtype == np.uint16:   # bf16 bit patterns
+        return SRC["bf16"]
+    raise TypeError("src must be float32 or uint16 (bf16 bits), got %s" % src.dtype)
+
+
+def quantize(src: np.ndarray, fmt: str, axis: int = 0):
+    """Quantize a 2-D array (float32, or uint16 holding bf16 bits).
+
+    axis=0: 1x32 groups along each row; returns codes [rows][Kp], scales [rows][Kp/32].
+    axis=1: 32x1 groups down each column, stored transposed: codes [cols][Kp], scales
+            [cols][Kp/32] with K = rows.
+    """
+    src = np.ascontiguousarray(src)
+    rows, cols = src.shape
+    L, K = (rows, cols) if axis == 0 else (cols, rows)
+    Kp = 32 * ((K + 31) // 32)
+    codes = np.zeros((L, max(Kp, 1)), dtype=np.uint8)
+    scales = np.zeros((L, max(Kp // 32, 1)), dtype=np.uint8)
+    if L > 0 and K > 0:
+        lib().mxo_quantize(_ptr(src), _src_type(src), rows, cols, cols, axis, FMT[fmt],
+                           _ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1])
+    return codes[:, :Kp], scales[:, :Kp // 32]
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str, K: int, out: str = "f32"):
+    """Reconstruct x_hat = dec(code) * 2^(s-127); returns float32 or uint16 (bf16 bits)."""
+    codes = np.ascontiguousarray(codes)
+    scales = np.ascontiguousarray(scales)
+    L = codes.shape[0]
+    dst = np.zeros((L, K), dtype=np.float32 if out == "f32" else np.uint16)
+    if L > 0 and K > 0:
+        lib().mxo_dequantize(_ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1], FMT[fmt],
+                             L, K, _ptr(dst), SRC[out], K)
+    return dst
+
+
+def gemm(x_codes, x_scales, x_fmt, w_codes, w_scales, w_fmt, K, alpha=1.0, bias=None):
+    """FP64 reference Y[M][N] and bound T[M][N]; W is given as rows w_codes[N][Kp]."""
+    xc = np.ascontiguousarray(x_codes)
+    xs = np.ascontiguousarray(x_scales)
+    wc = np.ascontiguousarray(w_codes)
+    ws = np.ascontiguousarray(w_scales)
+    M, N = xc.shape[0], wc.shape[0]
+    y = np.zeros((M, N), dtype=np.float64)
+    t = np.zeros((M, N), dtype=np.float64)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    if M > 0 and N > 0:
+        lib().mxo_gemm(M, N, K, _ptr(xc), xc.shape[1], _ptr(xs), xs.shape[1], FMT[x_fmt],
+                       _ptr(wc), wc.shape[1], _ptr(ws), ws.shape[1], FMT[w_fmt], float(alpha),
+                       _ptr(b), _ptr(y), _ptr(t))
+    return y, t
+
+
+def gemm_sampled(x_codes, x_scales, x_fmt, w_codes, w_scales, w_fmt, K, ii, jj, alpha=1.0,
+                 bias=None):
+    """Reference for the output elements (ii[s], jj[s]) only; returns (y[n], t[n])."""
+    xc = np.ascontiguousarray(x_codes)
+    xs = np.ascontiguousarray(x_scales)
+    wc = np.ascontiguousarray(w_codes)
+    ws = np.ascontiguousarray(w_scales)
+    ii = np.ascontiguousarray(ii, dtype=np.int64)
+    jj = np.ascontiguousarray(jj, dtype=np.int64)
+    n = ii.shape[0]
+    y = np.zeros(n, dtype=np.float64)
+    t = np.zeros(n, dtype=np.float64)
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    if n > 0:
+        lib().mxo_gemm_sampled(K, _ptr(xc), xc.shape[1], _ptr(xs), xs.shape[1], FMT[x_fmt],
+                               _ptr(wc), wc.shape[1], _ptr(ws), ws.shape[1], FMT[w_fmt],
+                               float(alpha), _ptr(b), n, _ptr(ii), _ptr(jj), _ptr(y), _ptr(t))
+    return y, t

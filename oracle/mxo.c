@@ -1,0 +1,339 @@
+/*
+ * mxo.c -- CPU oracle for OCP-MX block-scaled FP8 (MXFP8) quantize, dequantize and GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call this
+ * file: only the test suite, the smoke check and the benchmark's CPU-baseline leg use it.
+ * It shares no code, header, table or constant generator with the HIP library; it is
+ * plain C99 built with gcc, and it is deliberately slow and literal.
+ *
+ * Sources (page titles; sections in quotes):
+ *   [LPGP] "Low-Precision GPU Programming" (leetllm.com)
+ *     - "Format taxonomy: range, spacing, and bitfields": E4M3 max 448, no infinities,
+ *       0x7F/0xFF NaN, min normal 2^-6, subnormals down to 2^-9; E5M2 smallest subnormal
+ *       2^-16, largest finite 57,344.
+ *     - "Numerical hazards" / "Subnormals and flush-to-zero": round-to-nearest-even,
+ *       0.75*2^-9 -> 2^-9, 0.5*2^-9 -> signed zero.
+ *     - "Numerical hazards" / "Saturation cliffs": conversion rounds first, then a
+ *       saturating conversion clamps to +-448 / +-57,344.
+ *     - "Scale ownership and the GEMM dataflow": Y = XW, X in R^{MxK}, W in R^{KxN};
+ *       with block scaling along K the block-scale product stays inside the outer sum
+ *       over blocks b, a partial final block is zero-padded.
+ *     - "Scaling architectures" / "One letter, two reciprocal conventions": S is the
+ *       reconstruction scale, x_hat = S*q, q = Q(x/S); a zero-only group takes S = 1.
+ *     - "Microscaling: the two-row experiment": 32-element blocks, E8M0 byte c means
+ *       2^(c-127), 255 is NaN; the conservative power-of-two scale rounds amax/448
+ *       upward (exponent = max(-127, ceil(log2(amax/fmax)))), zero block -> 1.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the design notes):
+ *   - E5M2 uses the same scale rule with fmax = 57,344.
+ *   - A block containing NaN or +-Inf gets scale byte 255 and every code 0x7F.
+ *   - Padding positions (k >= K inside the last block) get code 0x00.
+ *   - The GEMM epilogue is y = alpha*acc + bias[j] (scale, then bias), done in FP64 here.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#include <float.h>
+
+#define MXO_F32 0
+#define MXO_BF16 1
+#define MXO_FMT_E4M3 0
+#define MXO_FMT_E5M2 1
+
+/* ---------------------------------------------------------------- decode ---------- */
+
+/* FP8 decode straight from the bitfields [LPGP "Format taxonomy"]:
+ *   E4M3: sign | 4 exponent bits (bias 7) | 3 mantissa bits; exponent 0 is subnormal
+ *         (0.m * 2^-6); S.1111.111 is NaN; there is no infinity.
+ *   E5M2: sign | 5 exponent bits (bias 15) | 2 mantissa bits; exponent 0 is subnormal
+ *         (0.m * 2^-14); exponent 31 is Inf (m = 0) or NaN.                               */
+double mxo_decode(uint8_t code, int fmt)
+{
+    int s = (code >> 7) & 1;
+    double mag;
+    if (fmt == MXO_FMT_E4M3) {
+        int E = (code >> 3) & 0xF, m = code & 0x7;
+        if (E == 15 && m == 7) return NAN;
+        if (E == 0) mag = ldexp((double)m / 8.0, -6);
+        else        mag = ldexp(1.0 + (double)m / 8.0, E - 7);
+    } else {
+        int E = (code >> 2) & 0x1F, m = code & 0x3;
+        if (E == 31) { if (m == 0) return s ? -INFINITY : INFINITY; return NAN; }
+        if (E == 0) mag = ldexp((double)m / 4.0, -14);
+        else        mag = ldexp(1.0 + (double)m / 4.0, E - 15);
+    }
+    return s ? -mag : mag;
+}
+
+/* E8M0 scale byte [LPGP "Microscaling: the two-row experiment"]: c in 0..254 is 2^(c-127),
+ * 255 is NaN; there is no zero, sign or infinity.                                          */
+double mxo_decode_e8m0(uint8_t c)
+{
+    if (c == 255) return NAN;
+    return ldexp(1.0, (int)c - 127);
+}
+
+/* Largest finite magnitude of each element format [LPGP "Format taxonomy"]. */
+double mxo_fmax(int fmt) { return fmt == MXO_FMT_E4M3 ? 448.0 : 57344.0; }
+
+/* ---------------------------------------------------------------- encode ---------- */
+
+/* Table of the finite non-negative magnitudes, indexed by code.  Because the sign bit is
+ * the top bit and exponent sits above mantissa, codes 0x00.. increase with magnitude:
+ * E4M3 0x00..0x7E (127 values; 0x7F is NaN), E5M2 0x00..0x7B (124 values; 0x7C is Inf). */
+static double g_mag[2][128];
+static int g_nmag[2];
+static int g_ready;
+
+static void build_tables(void)
+{
+    if (g_ready) return;
+    for (int f = 0; f < 2; ++f) {
+        int n = 0;
+        for (int c = 0; c < 128; ++c) {
+            double v = mxo_decode((uint8_t)c, f);
+            if (!isfinite(v)) break;
+            g_mag[f][n++] = v;
+        }
+        g_nmag[f] = n;
+    }
+    g_ready = 1;
+}
+
+int mxo_num_finite_codes(int fmt) { build_tables(); return g_nmag[fmt]; }
+
+/* Round-to-nearest-even, saturating conversion of an exact real value a to an FP8 code
+ * [LPGP "Subnormals and flush-to-zero", "Saturation cliffs"].
+ *   - |a| at or above fmax gives fmax (rounding first, then saturation, can only land
+ *     there: every finite value above fmax either rounds to fmax or overflows).
+ *   - otherwise find neighbours lo <= |a| < hi in the table and compare |a| with their
+ *     exact midpoint; a tie goes to the even code (mantissa LSB 0), also across the
+ *     subnormal/normal seam.
+ *   - the sign bit is copied from a, so -0 and negative values that round to zero give
+ *     0x80 (signed zero).
+ *   - NaN gives 0x7F (the NaN code of both formats with the sign bit clear).            */
+uint8_t mxo_encode(double a, int fmt)
+{
+    build_tables();
+    if (isnan(a)) return 0x7F;
+    uint8_t sign = signbit(a) ? 0x80 : 0x00;
+    double x = fabs(a);
+    int n = g_nmag[fmt];
+    const double *t = g_mag[fmt];
+    if (x >= t[n - 1]) return (uint8_t)(sign | (n - 1));
+    /* binary search: largest i with t[i] <= x (t[0] = 0 <= x always) */
+    int lo = 0, hi = n - 1;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (t[mid] <= x) lo = mid; else hi = mid;
+    }
+    /* now t[lo] <= x < t[hi] with hi = lo + 1 */
+    double midpoint = (t[lo] + t[hi]) / 2.0; /* exact: both are short dyadic rationals */
+    int code;
+    if (x < midpoint)      code = lo;
+    else if (x > midpoint) code = hi;
+    else                   code = (lo % 2 == 0) ? lo : hi;
+    return (uint8_t)(sign | code);
+}
+
+/* ---------------------------------------------------------------- scale rule ------ */
+
+/* Conservative power-of-two block scale [LPGP "Microscaling: the two-row experiment";
+ * "One letter, two reciprocal conventions"]:
+ *   amax == 0         -> S = 1            (byte 127)
+ *   amax non-finite   -> byte 255 (NaN)
+ *   otherwise         -> S = 2^e with e the smallest integer >= -127 such that
+ *                        amax <= fmax * 2^e; byte = e + 127.
+ * Written as the literal search; fmax*2^e and the comparison are exact in FP64.         */
+int mxo_scale_byte(double amax, int fmt)
+{
+    if (!isfinite(amax)) return 255;
+    if (amax == 0.0) return 127;
+    double fmax = mxo_fmax(fmt);
+    int e = -127;
+    while (ldexp(fmax, e) < amax) ++e;
+    return e + 127;
+}
+
+/* ---------------------------------------------------------------- helpers --------- */
+
+static double load_elem(const void *src, int src_type, int64_t idx)
+{
+    if (src_type == MXO_F32) return (double)((const float *)src)[idx];
+    uint16_t h = ((const uint16_t *)src)[idx];
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* bf16 round-to-nearest-even of an FP64 value, by neighbour search: bf16 has 7 stored
+ * mantissa bits and fp32's exponent range, so between 2^E and 2^(E+1) (E >= -126) the
+ * spacing is 2^(E-7), and below 2^-126 it is 2^-133.  Returns the bf16 bit pattern.    */
+uint16_t mxo_round_bf16(double v)
+{
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isinf(a)) return sign | 0x7F80;
+    if (a == 0.0) return sign;
+    int E;
+    frexp(a, &E);        /* a = f * 2^E, f in [0.5, 1) -> a in [2^(E-1), 2^E) */
+    E -= 1;              /* a in [2^E, 2^(E+1)) */
+    int q = (E < -126) ? -133 : E - 7;
+    double spacing = ldexp(1.0, q);
+    double lo = floor(a / spacing) * spacing;
+    double hi = lo + spacing;
+    double r;
+    if (a - lo < hi - a)      r = lo;
+    else if (a - lo > hi - a) r = hi;
+    else                      r = (fmod(lo / spacing, 2.0) == 0.0) ? lo : hi;
+    if (r >= ldexp(1.0, 128)) return sign | 0x7F80;       /* rounds past the top: Inf */
+    float f = (float)r;   /* r is a bf16 value, so it is exact in fp32 */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* fp32 rounding of an FP64 value that is exactly a (code * power of two): exact unless it
+ * is at or beyond 2^128, where IEEE round-to-nearest overflows to Inf.                   */
+static float to_f32(double v)
+{
+    if (isnan(v)) return NAN;
+    if (fabs(v) >= ldexp(1.0, 128)) return signbit(v) ? -INFINITY : INFINITY;
+    return (float)v;
+}
+
+/* ---------------------------------------------------------------- quantize -------- */
+
+/* Quantize one line of K values (element k at src[base + k*stride]) into ceil(K/32)
+ * blocks [LPGP "Scale ownership and the GEMM dataflow": block index b along K; partial
+ * final block zero-padded].                                                              */
+static void quantize_line(const void *src, int src_type, int64_t base, int64_t stride, int64_t K,
+                          int fmt, uint8_t *codes, uint8_t *scales)
+{
+    int64_t nb = (K + 31) / 32;
+    for (int64_t b = 0; b < nb; ++b) {
+        int64_t k0 = 32 * b, k1 = k0 + 32 < K ? k0 + 32 : K;
+        double amax = 0.0;
+        int nonfinite = 0;
+        for (int64_t k = k0; k < k1; ++k) {
+            double x = load_elem(src, src_type, base + k * stride);
+            if (!isfinite(x)) nonfinite = 1;
+            else if (fabs(x) > amax) amax = fabs(x);
+        }
+        if (nonfinite) {
+            scales[b] = 255;
+            for (int64_t k = k0; k < k0 + 32; ++k) codes[k] = 0x7F;
+            continue;
+        }
+        int sb = mxo_scale_byte(amax, fmt);
+        scales[b] = (uint8_t)sb;
+        int e = sb - 127;
+        for (int64_t k = k0; k < k0 + 32; ++k) {
+            if (k < K) {
+                double x = load_elem(src, src_type, base + k * stride);
+                codes[k] = mxo_encode(ldexp(x, -e), fmt);  /* x / S, exact in FP64 */
+            } else {
+                codes[k] = 0x00;                            /* zero padding */
+            }
+        }
+    }
+}
+
+/* axis 0 (rowwise): the lines are the rows of src [rows][ld_src], K = cols.
+ * axis 1 (colwise): the lines are the columns of src, K = rows, and the output is stored
+ *                   transposed, codes [cols][ld_codes], scales [cols][ld_scales].
+ * Writes Kp = 32*ceil(K/32) codes and Kp/32 scale bytes per line.                        */
+void mxo_quantize(const void *src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
+                  int axis, int fmt, uint8_t *codes, int64_t ld_codes, uint8_t *scales,
+                  int64_t ld_scales)
+{
+    build_tables();
+    int64_t L = axis == 0 ? rows : cols;
+    int64_t K = axis == 0 ? cols : rows;
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t l = 0; l < L; ++l) {
+        int64_t base = axis == 0 ? l * ld_src : l;
+        int64_t stride = axis == 0 ? 1 : ld_src;
+        quantize_line(src, src_type, base, stride, K, fmt, codes + l * ld_codes,
+                      scales + l * ld_scales);
+    }
+}
+
+/* ---------------------------------------------------------------- dequantize ------ */
+
+/* x_hat = dec(code) * 2^(s-127) [LPGP "One letter, two reciprocal conventions":
+ * reconstruction x_hat = S*q], computed exactly in FP64 then rounded to the destination:
+ * fp32 (exact unless past 2^128 -> Inf) or bf16 (RNE).  dst_type 0 = fp32, 1 = bf16.   */
+void mxo_dequantize(const uint8_t *codes, int64_t ld_codes, const uint8_t *scales,
+                    int64_t ld_scales, int fmt, int64_t L, int64_t K, void *dst, int dst_type,
+                    int64_t ld_dst)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t l = 0; l < L; ++l) {
+        for (int64_t k = 0; k < K; ++k) {
+            double v = mxo_decode(codes[l * ld_codes + k], fmt) *
+                       mxo_decode_e8m0(scales[l * ld_scales + k / 32]);
+            if (dst_type == MXO_F32) ((float *)dst)[l * ld_dst + k] = to_f32(v);
+            else ((uint16_t *)dst)[l * ld_dst + k] = mxo_round_bf16(v);
+        }
+    }
+}
+
+/* ---------------------------------------------------------------- GEMM ------------ */
+
+/* One output element of the block-K scaled contraction [LPGP "Scale ownership and the
+ * GEMM dataflow"]:
+ *   acc = sum_b  S_X[i,b] * S_W[b,j] * sum_{k in b, k < K} Xq[i,k] * Wq[k,j]
+ *   y   = alpha * acc + bias[j]
+ * and the bound T = |alpha| * sum_b S_X S_W sum_k |Xq Wq|.  W is given column-major,
+ * i.e. as rows w_codes[j][k] (the kernel contract's "col_major_packed" operand).
+ * Every product of two FP8 values and two powers of two is exact in FP64.               */
+static void gemm_one(int64_t i, int64_t j, int64_t K,
+                     const uint8_t *xc, int64_t ld_x, const uint8_t *xs, int64_t ld_xs, int xf,
+                     const uint8_t *wc, int64_t ld_w, const uint8_t *ws, int64_t ld_ws, int wf,
+                     double alpha, const float *bias, double *y, double *t)
+{
+    int64_t nb = (K + 31) / 32;
+    double acc = 0.0, bound = 0.0;
+    for (int64_t b = 0; b < nb; ++b) {
+        double inner = 0.0, inner_abs = 0.0;
+        for (int64_t k = 32 * b; k < 32 * b + 32 && k < K; ++k) {
+            double p = mxo_decode(xc[i * ld_x + k], xf) * mxo_decode(wc[j * ld_w + k], wf);
+            inner += p;
+            inner_abs += fabs(p);
+        }
+        double sprod = mxo_decode_e8m0(xs[i * ld_xs + b]) * mxo_decode_e8m0(ws[j * ld_ws + b]);
+        acc += sprod * inner;
+        bound += sprod * inner_abs;
+    }
+    *y = alpha * acc + (bias ? (double)bias[j] : 0.0);
+    *t = fabs(alpha) * bound;
+}
+
+/* Full reference: y_ref and t are dense [M][N] row-major FP64. */
+void mxo_gemm(int64_t M, int64_t N, int64_t K,
+              const uint8_t *x_codes, int64_t ld_x, const uint8_t *x_scales, int64_t ld_xs, int x_fmt,
+              const uint8_t *w_codes, int64_t ld_w, const uint8_t *w_scales, int64_t ld_ws, int w_fmt,
+              double alpha, const float *bias, double *y_ref, double *t)
+{
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < N; ++j)
+            gemm_one(i, j, K, x_codes, ld_x, x_scales, ld_xs, x_fmt, w_codes, ld_w, w_scales,
+                     ld_ws, w_fmt, alpha, bias, &y_ref[i * N + j], &t[i * N + j]);
+}
+
+/* Sampled reference: n output elements (ii[s], jj[s]). */
+void mxo_gemm_sampled(int64_t K,
+                      const uint8_t *x_codes, int64_t ld_x, const uint8_t *x_scales, int64_t ld_xs, int x_fmt,
+                      const uint8_t *w_codes, int64_t ld_w, const uint8_t *w_scales, int64_t ld_ws, int w_fmt,
+                      double alpha, const float *bias, int64_t n, const int64_t *ii, const int64_t *jj,
+                      double *y_ref, double *t)
+{
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t s = 0; s < n; ++s)
+        gemm_one(ii[s], jj[s], K, x_codes, ld_x, x_scales, ld_xs, x_fmt, w_codes, ld_w, w_scales,
+                 ld_ws, w_fmt, alpha, bias, &y_ref[s], &t[s]);
+}
