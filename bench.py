@@ -1,0 +1,217 @@
+"""Benchmark of the MXFP8 hot path on one MI355X.
+
+One step = the whole path over one batch of the projection workload (M=8192, K=4096,
+N=4096, bf16 activations ~N(0,1) with 0.1% outliers x100, bf16 weights ~N(0,0.02)):
+    mxq_quantize(X) rowwise E4M3 -> mxq_quantize(W) rowwise E4M3 -> mxq_gemm (bf16 out).
+Inputs are resident in HBM before timing starts.  `value` is the whole step's
+throughput, 2*M*N*K / step time, in TFLOP/s.  The dominant kernel (the GEMM) is also
+timed on its own with HIP events around each of its launches inside the timed region
+(the events sit on the stream the kernels are launched on) and reported against the
+dense MXFP8 matrix-core peak; the standalone quantize of 2^28 bf16 elements is reported
+against the HBM peak.  The CPU oracle is timed on a bounded sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MXFP8_TFLOPS = 5000.0      # MI355X dense FP8 / MXFP8 matrix-core peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    return p.parse_args()
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters (see profiles/), or None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        return t.get(kernel)
+    except (OSError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp8_block_scaled_03_amd as mxq
+    from mxfp8_block_scaled_03_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mxq.lib()
+
+    d = wl.workload2()
+    M, K, N = d["M"], d["K"], d["N"]
+    x = d["x"].to(dev)
+    w = d["w"].to(dev)
+    Kp = 32 * ((K + 31) // 32)
+    xc = torch.empty((M, Kp), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M, Kp // 32), dtype=torch.uint8, device=dev)
+    wc = torch.empty((N, Kp), dtype=torch.uint8, device=dev)
+    ws = torch.empty((N, Kp // 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        mxq.quantize(x, "e4m3", "row", codes=xc, scales=xs)
+        mxq.quantize(w, "e4m3", "row", codes=wc, scales=ws)
+        if ev is not None:
+            ev[0].record(stream)
+        mxq.gemm(xc, xs, wc, ws, K, out=y)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    gemm_events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(gemm_events[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    gemm_ms = [a.elapsed_time(b) for a, b in gemm_events]
+    gemm_ms_avg = sum(gemm_ms) / len(gemm_ms)
+    flops = 2.0 * M * N * K
+    value = flops / (ms_step * 1e-3) / 1e12
+    gemm_tflops = flops / (gemm_ms_avg * 1e-3) / 1e12
+    gemm_bytes = (M + N) * Kp * (1 + 1 / 32) + M * N * 2
+
+    # ---- standalone quantize: 2^28 bf16 elements, rowwise E4M3 (HBM-bound)
+    q = wl.workload_q()
+    qx = q["x"].to(dev)
+    del q
+    qc = torch.empty((qx.shape[0], qx.shape[1]), dtype=torch.uint8, device=dev)
+    qs = torch.empty((qx.shape[0], qx.shape[1] // 32), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        mxq.quantize(qx, "e4m3", "row", codes=qc, scales=qs)
+    torch.cuda.synchronize()
+    nq = 20
+    qe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nq)]
+    for a, b in qe:
+        a.record(stream)
+        mxq.quantize(qx, "e4m3", "row", codes=qc, scales=qs)
+        b.record(stream)
+    torch.cuda.synchronize()
+    q_ms = sum(a.elapsed_time(b) for a, b in qe) / nq
+    q_bytes = qx.numel() * (2 + 1 + 1 / 32)
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+    del qx, qc, qs
+
+    # quantize of the step's X alone (8192 x 4096 bf16)
+    xq_e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for a, b in xq_e:
+        a.record(stream)
+        mxq.quantize(x, "e4m3", "row", codes=xc, scales=xs)
+        b.record(stream)
+    torch.cuda.synchronize()
+    xq_ms = sum(a.elapsed_time(b) for a, b in xq_e) / len(xq_e)
+    xq_gbs = M * K * (2 + 1 + 1 / 32) / (xq_ms * 1e-3) / 1e9
+
+    traffic = load_traffic("gemm")
+    out = {
+        "metric": "MXFP8 GEMM TFLOP/s (% dense MFMA peak); mx_quantize GB/s (% HBM peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (MXFP8, E8M0 block scales), fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "projection GEMM M=8192 K=4096 N=4096: bf16 X ~N(0,1) with 0.1% x100, "
+                               "bf16 W ~N(0,0.02); quantize X and W rowwise to MXFP8 E4M3, GEMM with bf16 output",
+                   "M": M, "K": K, "N": N, "step": "quantize(X) + quantize(W) + gemm"},
+        "roofline": {"bound": "mfma", "kernel": "mxq gemm (k_gemm)", "achieved": round(gemm_tflops, 2),
+                     "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MXFP8_TFLOPS, 4),
+                     "traffic": traffic, "algorithmic_bytes": int(gemm_bytes), "ms_avg": round(gemm_ms_avg, 5)},
+        "components": {
+            "gemm": {"ms": round(gemm_ms_avg, 5), "tflops": round(gemm_tflops, 2)},
+            "quantize_x": {"ms": round(xq_ms, 5), "gbs": round(xq_gbs, 1), "bytes": int(M * K * 3.03125)},
+            "quantize_2p28": {"ms": round(q_ms, 5), "gbs": round(q_gbs, 1), "frac_hbm": round(q_gbs / PEAK_HBM_GBS, 4),
+                              "bytes": int(q_bytes), "workload": "[16384][16384] bf16 Laplace(0,1) 1% x1e4, rowwise E4M3"},
+        },
+    }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(d, xc, xs, wc, ws, M, N, K, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+def cpu_baseline(d, xc, xs, wc, ws, M, N, K, target_s):
+    """Time the oracle on a bounded sample of the same step and scale to TFLOP/s:
+    quantize of a row slice of X and W, and the FP64 reference of a sample of outputs."""
+    import numpy as np
+
+    import oracle
+    from mxfp8_block_scaled_03_amd.workloads import bf16_bits
+
+    x_bits = bf16_bits(d["x"])
+    w_bits = bf16_bits(d["w"])
+    rows = 512
+    t = time.perf_counter()
+    oracle.quantize(x_bits[:rows], "e4m3")
+    tq = time.perf_counter() - t
+    quant_per_elem = tq / (rows * K)
+    xc_h, xs_h, wc_h, ws_h = xc.cpu().numpy(), xs.cpu().numpy(), wc.cpu().numpy(), ws.cpu().numpy()
+    rng = np.random.default_rng(0)
+    n = 2048
+    ii, jj = rng.integers(0, M, n), rng.integers(0, N, n)
+    t = time.perf_counter()
+    oracle.gemm_sampled(xc_h, xs_h, "e4m3", wc_h, ws_h, "e4m3", K, ii, jj)
+    tg = time.perf_counter() - t
+    per_out = tg / n
+    # grow the GEMM sample to roughly the target time
+    n2 = int(min(max(target_s / max(per_out, 1e-9) * 0.8, n), 1 << 22))
+    ii, jj = rng.integers(0, M, n2), rng.integers(0, N, n2)
+    t = time.perf_counter()
+    oracle.gemm_sampled(xc_h, xs_h, "e4m3", wc_h, ws_h, "e4m3", K, ii, jj)
+    tg2 = time.perf_counter() - t
+    per_out = tg2 / n2
+    step_s = quant_per_elem * (M * K + N * K) + per_out * M * N
+    del w_bits
+    return {"value": round(2.0 * M * N * K / step_s / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "oracle quantize of %d of the %d X rows and FP64 reference of %d of the %d outputs "
+                      "(%.1f s CPU); step time extrapolated per element" % (rows, M, n2, M * N, tq + tg2),
+            "step_seconds_extrapolated": round(step_s, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * mxq.h -- C ABI of the MI355X (gfx950) MXFP8 library: OCP-MX block-scaled FP8
+ * quantize, dequantize and GEMM  Y = X W.
+ *
+ * Sources ("Low-Precision GPU Programming", leetllm.com):
+ *   - "Scale ownership and the GEMM dataflow": Y = X W with X in R^{M x K}, W in R^{K x N};
+ *     every element is a positive scale times a low-precision code; with 32-element
+ *     microscaling along K the product of the two block scales stays inside the sum
+ *     over blocks, and a partial final block is zero-padded.  A consumer may apply the
+ *     scales inside the GEMM; standalone dequantization is kept for debugging/fallback.
+ *   - "Microscaling: the two-row experiment": 32-element blocks, one E8M0 scale byte per
+ *     block (byte c means 2^(c-127), 255 is NaN); the block scale is the power of two
+ *     obtained by rounding amax/fmax upward, clamped at 2^-127, and 1 for a zero block.
+ *   - "Numerical hazards": round-to-nearest-even, saturating conversion to +-448 (E4M3)
+ *     or +-57,344 (E5M2); subnormal codes are kept (no flush to zero).
+ *   - "Hardware support and kernel ABI contracts": the kernel contract record -- X
+ *     row-major with 1x32 groups along K, W column-major ("col_major_packed") with 32x1
+ *     groups along K, E8M0 scales, FP32 accumulation, scales applied inside the block
+ *     contraction, epilogue bias (FP32) then output cast, RNE, saturate; dtype tags,
+ *     scales, orientation and padding are passed together.
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library never
+ *     allocates, frees or synchronizes; work is enqueued on `stream` (a hipStream_t
+ *     passed as void*; NULL means the default stream) and runs asynchronously.
+ *   - Sizes and leading dimensions are in ELEMENTS of the pointed-to type (bytes for
+ *     code and scale arrays).  K is the contraction (block) axis, Kp = 32*ceil(K/32)
+ *     and nb = Kp/32 is the number of blocks per line.
+ *   - Return value: MXQ_OK (0) or a negative mxq_status.  All argument validation runs
+ *     on the host before anything is enqueued; an invalid call enqueues nothing and
+ *     never aborts.  A HIP launch error is reported as MXQ_ERR_HIP; a device fault
+ *     surfaces at the caller's next synchronization.
+ *   - A call with an empty problem (a zero dimension) validates its arguments and
+ *     returns MXQ_OK without enqueuing work (mxq_gemm with K = 0 still writes
+ *     Y = bias, or zeros).
+ *   - Codes are raw OCP bytes (never the FNUZ encoding): E4M3 bias 7, NaN 0x7F/0xFF;
+ *     E5M2 bias 15.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXQ_OK = 0,
+  MXQ_ERR_NULL = -1,   /* a required pointer is NULL                              */
+  MXQ_ERR_SHAPE = -2,  /* a negative dimension, or a size that overflows int64     */
+  MXQ_ERR_LD = -3,     /* a leading dimension smaller than the row it must hold    */
+  MXQ_ERR_ALIGN = -4,  /* a pointer or leading dimension breaks the stated alignment */
+  MXQ_ERR_DTYPE = -5,  /* a dtype tag that the entry point does not accept         */
+  MXQ_ERR_ARG = -6,    /* any other invalid argument (axis, non-finite alpha)      */
+  MXQ_ERR_HIP = -7     /* the HIP runtime reported an error when enqueuing          */
+} mxq_status;
+
+typedef enum {
+  MXQ_F32 = 0,   /* IEEE binary32                                       */
+  MXQ_BF16 = 1,  /* bfloat16 (upper half of binary32), stored as 2 bytes */
+  MXQ_E4M3 = 2,  /* OCP FP8 E4M3 element code (forward operands)        */
+  MXQ_E5M2 = 3   /* OCP FP8 E5M2 element code (gradients)               */
+} mxq_dtype;
+
+typedef enum {
+  MXQ_ROWWISE = 0, /* 1x32 groups along each row: lines = rows, K = cols             */
+  MXQ_COLWISE = 1  /* 32x1 groups down each column, output transposed: lines = cols,
+                      K = rows (requantized from the wide source, not byte-transposed) */
+} mxq_axis;
+
+/*
+ * mxq_quantize -- MX block quantization of a 2-D bf16/fp32 matrix.
+ *
+ * src      [rows][ld_src] row-major, src_type MXQ_F32 or MXQ_BF16, ld_src >= cols.
+ *          Any element alignment is accepted; 16-byte aligned rows take the fast path.
+ * axis     MXQ_ROWWISE: line l = row l, K = cols.
+ *          MXQ_COLWISE: line l = column l, K = rows.
+ * elem     MXQ_E4M3 or MXQ_E5M2 (fmax 448 or 57,344).
+ * codes    [L][ld_codes] bytes, ld_codes >= Kp, ld_codes % 16 == 0, pointer 16-byte
+ *          aligned.  For each line, codes[l][0..Kp) are written; positions K..Kp-1 of
+ *          the last block get 0x00 (zero padding); codes[l][Kp..ld_codes) are untouched.
+ * scales   [L][ld_scales] bytes, ld_scales >= nb; scales[l][b] is the E8M0 byte of block b.
+ *
+ * Per block b of a line (elements 32b .. min(32b+32, K)-1):
+ *   amax = max |x|;  scale byte = 127 if amax == 0, else e + 127 with e the smallest
+ *   integer >= -127 such that amax <= fmax * 2^e;  code = RNE-satfinite(x * 2^-e), the
+ *   sign copied from x (so -0 and negative underflow give 0x80).
+ *   A block holding NaN or Inf gets scale byte 255 and every code 0x7F.
+ * The result is bit-exact; it does not depend on the launch configuration.
+ */
+int mxq_quantize(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
+                 int axis, int elem, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                 int64_t ld_scales, void* stream);
+
+/*
+ * mxq_dequantize -- reconstruction x_hat = dec(code) * 2^(s-127) (debug / fallback path).
+ *
+ * codes    [L][ld_codes] bytes (ld_codes >= K), scales [L][ld_scales] (ld_scales >= nb).
+ * elem     MXQ_E4M3 or MXQ_E5M2.
+ * dst      [L][ld_dst] of dst_type MXQ_F32 (exact; values at or beyond 2^128 become Inf)
+ *          or MXQ_BF16 (round-to-nearest-even), ld_dst >= K, pointer aligned to its
+ *          element size.  Scale byte 255 and NaN codes give NaN.
+ */
+int mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                   int64_t ld_scales, int elem, int64_t L, int64_t K, void* dst, int dst_type,
+                   int64_t ld_dst, void* stream);
+
+/*
+ * mxq_gemm -- block-scaled FP8 GEMM  Y = alpha * (X W) + bias.
+ *
+ * X        x_codes [M][ld_x] (row-major, K contiguous), x_scales [M][ld_xs] E8M0,
+ *          x_elem MXQ_E4M3 or MXQ_E5M2.
+ * W        w_codes [N][ld_w]: W stored column-major, i.e. column j of the K x N matrix
+ *          is the contiguous row w_codes[j][0..K) (this is what mxq_quantize gives for
+ *          an [N][K] weight with MXQ_ROWWISE, or a [K][N] weight with MXQ_COLWISE);
+ *          w_scales [N][ld_ws], w_elem MXQ_E4M3 or MXQ_E5M2 (mixed formats allowed).
+ *          ld_x, ld_w >= Kp and multiples of 16; code pointers 16-byte aligned;
+ *          ld_xs, ld_ws >= nb.
+ * Result   acc[i][j] = sum_b 2^(sx[i][b] + sw[j][b] - 254) * sum_{k in b, k < K}
+ *                        dec(x[i][k]) * dec(w[j][k])
+ *          accumulated in FP32 (the products and the per-block scaling are done by the
+ *          matrix cores; summation order is implementation-defined); code positions
+ *          k >= K are ignored.  Epilogue: y = alpha * acc (+ bias[j] if bias != NULL),
+ *          rounded once to y_type.
+ * bias     [N] FP32 device array or NULL.
+ * y        [M][ld_y] row-major, y_type MXQ_F32 or MXQ_BF16 (RNE), ld_y >= N, pointer
+ *          aligned to its element size.
+ * alpha    must be finite.
+ * Accuracy: |y - y_exact| <= 1e-5 * |alpha| * sum_k |scaled products| (plus one rounding
+ * of the bias add and of the output cast).
+ */
+int mxq_gemm(int64_t M, int64_t N, int64_t K,
+             const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_elem,
+             const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws, int w_elem,
+             float alpha, const float* bias, void* y, int y_type, int64_t ld_y, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* mxq_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mxq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

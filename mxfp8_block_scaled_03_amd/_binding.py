@@ -1,0 +1,168 @@
+"""ctypes binding of libmxq.so (include/mxq.h).  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(PKG, "libmxq.so")
+
+MXQ_F32, MXQ_BF16, MXQ_E4M3, MXQ_E5M2 = 0, 1, 2, 3
+MXQ_ROWWISE, MXQ_COLWISE = 0, 1
+
+_ELEM = {"e4m3": MXQ_E4M3, "e5m2": MXQ_E5M2}
+_AXIS = {"row": MXQ_ROWWISE, "col": MXQ_COLWISE, 0: MXQ_ROWWISE, 1: MXQ_COLWISE}
+
+
+class MxqError(ValueError):
+    """A negative mxq_status from the library (invalid arguments or a HIP launch error)."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%d)" % (where, mxq_status_string(status), status))
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libmxq.so; raises if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libmxq.so is not built (run __graft_entry__.build() or "
+                               "python -m mxfp8_block_scaled_03_amd.build)")
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.mxq_quantize.restype = ci
+        L.mxq_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, vp, i64, vp, i64, vp]
+        L.mxq_dequantize.restype = ci
+        L.mxq_dequantize.argtypes = [vp, i64, vp, i64, ci, i64, i64, vp, ci, i64, vp]
+        L.mxq_gemm.restype = ci
+        L.mxq_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, ci, vp, i64, vp, i64, ci,
+                               ctypes.c_float, vp, vp, ci, i64, vp]
+        L.mxq_status_string.restype = ctypes.c_char_p
+        L.mxq_status_string.argtypes = [ci]
+        L.mxq_version.restype = ci
+        L.mxq_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+# ----------------------------------------------------------------- raw C entry points
+
+def mxq_quantize(src, src_type, rows, cols, ld_src, axis, elem, codes, ld_codes, scales, ld_scales,
+                 stream=None) -> int:
+    return lib().mxq_quantize(src, src_type, rows, cols, ld_src, axis, elem, codes, ld_codes, scales,
+                              ld_scales, stream)
+
+
+def mxq_dequantize(codes, ld_codes, scales, ld_scales, elem, L, K, dst, dst_type, ld_dst, stream=None) -> int:
+    return lib().mxq_dequantize(codes, ld_codes, scales, ld_scales, elem, L, K, dst, dst_type, ld_dst, stream)
+
+
+def mxq_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws, w_elem,
+             alpha, bias, y, y_type, ld_y, stream=None) -> int:
+    return lib().mxq_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws,
+                          w_elem, alpha, bias, y, y_type, ld_y, stream)
+
+
+def mxq_status_string(status: int) -> str:
+    return lib().mxq_status_string(status).decode()
+
+
+def mxq_version() -> int:
+    return lib().mxq_version()
+
+
+# ----------------------------------------------------------------- torch conveniences
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise MxqError(status, where)
+
+
+def _wide_type(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return MXQ_F32
+    if t.dtype == torch.bfloat16:
+        return MXQ_BF16
+    raise TypeError("expected a float32 or bfloat16 tensor, got %s" % t.dtype)
+
+
+def _round_up(v: int, m: int) -> int:
+    return (v + m - 1) // m * m
+
+
+def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None):
+    """MX-quantize a 2-D bf16/fp32 CUDA tensor.
+
+    axis="row": 1x32 groups along each row -> codes [rows][Kp], scales [rows][Kp/32].
+    axis="col": 32x1 groups down each column, stored transposed -> codes [cols][Kp],
+                scales [cols][Kp/32] (K = rows).
+    Codes are uint8 OCP bytes; scales are uint8 E8M0 bytes.  Optional preallocated
+    outputs may be wider than Kp (their row stride is passed as the leading dimension).
+    """
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("quantize expects a 2-D tensor")
+    if x.stride(1) != 1:
+        raise ValueError("quantize expects unit stride along the last dimension")
+    rows, cols = x.shape
+    ax = _AXIS[axis]
+    L, K = (rows, cols) if ax == MXQ_ROWWISE else (cols, rows)
+    Kp = _round_up(K, 32)
+    if codes is None:
+        codes = torch.empty((L, Kp), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((L, Kp // 32), dtype=torch.uint8, device=x.device)
+    st = mxq_quantize(x.data_ptr(), _wide_type(x), rows, cols, x.stride(0) if rows > 0 else cols, ax,
+                      _ELEM[elem], codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0),
+                      _stream_handle())
+    _check(st, "mxq_quantize")
+    return codes, scales
+
+
+def dequantize(codes, scales, K: int, elem: str = "e4m3", out_dtype=None):
+    """Reconstruct dec(code) * 2^(s-127) as fp32 (default) or bf16, shape [L][K]."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.float32
+    L = codes.shape[0]
+    dst = torch.empty((L, K), dtype=out_dtype, device=codes.device)
+    st = mxq_dequantize(codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0), _ELEM[elem], L, K,
+                        dst.data_ptr(), _wide_type(dst), K, _stream_handle())
+    _check(st, "mxq_dequantize")
+    return dst
+
+
+def gemm(x_codes, x_scales, w_codes, w_scales, K: int, x_elem: str = "e4m3", w_elem: str = "e4m3",
+         alpha: float = 1.0, bias=None, out_dtype=None, out=None):
+    """Y[M][N] = alpha * (X W) + bias with X = (x_codes [M][Kp], x_scales) and W column-major
+    (w_codes [N][Kp], w_scales)."""
+    torch = _torch()
+    M, N = x_codes.shape[0], w_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=x_codes.device)
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N):
+        raise ValueError("bias must be a float32 tensor of N elements")
+    st = mxq_gemm(M, N, K, x_codes.data_ptr(), x_codes.stride(0), x_scales.data_ptr(), x_scales.stride(0),
+                  _ELEM[x_elem], w_codes.data_ptr(), w_codes.stride(0), w_scales.data_ptr(), w_scales.stride(0),
+                  _ELEM[w_elem], float(alpha), None if bias is None else bias.data_ptr(), out.data_ptr(),
+                  _wide_type(out), out.stride(0), _stream_handle())
+    _check(st, "mxq_gemm")
+    return out

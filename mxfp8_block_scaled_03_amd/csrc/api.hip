@@ -1,0 +1,115 @@
+// api.hip -- the C ABI declared in include/mxq.h: host-side argument validation and
+// dispatch to the gfx950 kernels.  Nothing here allocates, frees or synchronizes.
+#include "mxq.h"
+
+#include <math.h>
+
+#include "codec.hpp"
+#include "internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;    // M, N, rows, cols, K below 2^31
+constexpr int64_t kMaxCodeLd = (int64_t)1 << 24; // GEMM code leading dims (32-bit tile offsets)
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int to_fmt(int elem) { return elem == MXQ_E4M3 ? mxq::kE4M3 : mxq::kE5M2; }
+
+bool is_elem(int t) { return t == MXQ_E4M3 || t == MXQ_E5M2; }
+bool is_wide(int t) { return t == MXQ_F32 || t == MXQ_BF16; }
+
+// a * b fits in int64 for non-negative a, b
+bool mul_ok(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / a; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxq_status_string(int status) {
+  switch (status) {
+    case MXQ_OK: return "MXQ_OK";
+    case MXQ_ERR_NULL: return "MXQ_ERR_NULL: a required pointer is NULL";
+    case MXQ_ERR_SHAPE: return "MXQ_ERR_SHAPE: negative or too large dimension";
+    case MXQ_ERR_LD: return "MXQ_ERR_LD: leading dimension too small or too large";
+    case MXQ_ERR_ALIGN: return "MXQ_ERR_ALIGN: pointer or leading dimension misaligned";
+    case MXQ_ERR_DTYPE: return "MXQ_ERR_DTYPE: dtype tag not accepted here";
+    case MXQ_ERR_ARG: return "MXQ_ERR_ARG: invalid argument";
+    case MXQ_ERR_HIP: return "MXQ_ERR_HIP: HIP runtime error while enqueuing";
+    default: return "unknown mxq status";
+  }
+}
+
+int mxq_version(void) { return 100; }
+
+int mxq_quantize(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int axis, int elem,
+                 uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, void* stream) {
+  if (!is_wide(src_type) || !is_elem(elem)) return MXQ_ERR_DTYPE;
+  if (axis != MXQ_ROWWISE && axis != MXQ_COLWISE) return MXQ_ERR_ARG;
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return MXQ_ERR_SHAPE;
+  const int64_t L = axis == MXQ_ROWWISE ? rows : cols;
+  const int64_t K = axis == MXQ_ROWWISE ? cols : rows;
+  const int64_t Kp = 32 * ((K + 31) / 32), nb = Kp / 32;
+  if (L == 0 || K == 0) return MXQ_OK;
+  if (!src || !codes || !scales) return MXQ_ERR_NULL;
+  const int64_t es = src_type == MXQ_BF16 ? 2 : 4;
+  if (ld_src < cols || ld_codes < Kp || ld_scales < nb) return MXQ_ERR_LD;
+  if (!mul_ok(rows, ld_src * es) || !mul_ok(L, ld_codes) || !mul_ok(L, ld_scales)) return MXQ_ERR_SHAPE;
+  if (!aligned(src, (uintptr_t)es) || !aligned(codes, 16) || ld_codes % 16 != 0) return MXQ_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const bool src16 = aligned(src, 16) && (ld_src * es) % 16 == 0;
+  if (axis == MXQ_ROWWISE) {
+    const bool vec = src16 && K % 8 == 0;
+    const bool flat = vec && ld_src == K && K % 32 == 0 && ld_codes == Kp && ld_scales == nb;
+    return hip_status(mxq::launch_quant_rows(src, src_type == MXQ_BF16, rows, K, ld_src, to_fmt(elem), codes,
+                                             ld_codes, scales, ld_scales, flat, vec, st));
+  }
+  return hip_status(mxq::launch_quant_cols(src, src_type == MXQ_BF16, rows, cols, ld_src, to_fmt(elem), codes,
+                                           ld_codes, scales, ld_scales, src16, st));
+}
+
+int mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales, int64_t ld_scales, int elem,
+                   int64_t L, int64_t K, void* dst, int dst_type, int64_t ld_dst, void* stream) {
+  if (!is_elem(elem) || !is_wide(dst_type)) return MXQ_ERR_DTYPE;
+  if (L < 0 || K < 0 || L >= kMaxDim || K >= kMaxDim) return MXQ_ERR_SHAPE;
+  if (L == 0 || K == 0) return MXQ_OK;
+  if (!codes || !scales || !dst) return MXQ_ERR_NULL;
+  const int64_t nb = (K + 31) / 32;
+  const int64_t es = dst_type == MXQ_BF16 ? 2 : 4;
+  if (ld_codes < K || ld_scales < nb || ld_dst < K) return MXQ_ERR_LD;
+  if (!mul_ok(L, ld_codes) || !mul_ok(L, ld_dst * es) || !mul_ok(L, ld_scales)) return MXQ_ERR_SHAPE;
+  if (!aligned(dst, (uintptr_t)es)) return MXQ_ERR_ALIGN;
+  const bool vec = K % 8 == 0 && aligned(codes, 8) && ld_codes % 8 == 0 && aligned(dst, 16) && (ld_dst * es) % 16 == 0;
+  return hip_status(mxq::launch_dequant(codes, ld_codes, scales, ld_scales, to_fmt(elem), L, K, dst,
+                                        dst_type == MXQ_BF16, ld_dst, vec, (hipStream_t)stream));
+}
+
+int mxq_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales,
+             int64_t ld_xs, int x_elem, const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws,
+             int w_elem, float alpha, const float* bias, void* y, int y_type, int64_t ld_y, void* stream) {
+  if (!is_elem(x_elem) || !is_elem(w_elem) || !is_wide(y_type)) return MXQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxCodeLd) return MXQ_ERR_SHAPE;
+  if (!isfinite(alpha)) return MXQ_ERR_ARG;
+  if (M == 0 || N == 0) return MXQ_OK;
+  const int64_t Kp = 32 * ((K + 31) / 32), nb = Kp / 32;
+  if (!y) return MXQ_ERR_NULL;
+  if (K > 0 && (!x_codes || !x_scales || !w_codes || !w_scales)) return MXQ_ERR_NULL;
+  const int64_t ey = y_type == MXQ_BF16 ? 2 : 4;
+  if (ld_y < N) return MXQ_ERR_LD;
+  if (K > 0) {
+    if (ld_x < Kp || ld_w < Kp || ld_xs < nb || ld_ws < nb) return MXQ_ERR_LD;
+    if (ld_x >= kMaxCodeLd || ld_w >= kMaxCodeLd || ld_xs >= kMaxCodeLd / 2 || ld_ws >= kMaxCodeLd / 2)
+      return MXQ_ERR_LD;
+    if (!aligned(x_codes, 16) || !aligned(w_codes, 16) || ld_x % 16 != 0 || ld_w % 16 != 0) return MXQ_ERR_ALIGN;
+    if (!mul_ok(M, ld_x) || !mul_ok(N, ld_w) || !mul_ok(M, ld_xs) || !mul_ok(N, ld_ws)) return MXQ_ERR_SHAPE;
+  }
+  if (!mul_ok(M, ld_y * ey)) return MXQ_ERR_SHAPE;
+  if (!aligned(y, (uintptr_t)ey) || (bias && !aligned(bias, 4))) return MXQ_ERR_ALIGN;
+  return hip_status(mxq::launch_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, to_fmt(x_elem), w_codes, ld_w, w_scales,
+                                     ld_ws, to_fmt(w_elem), alpha, bias, y, y_type == MXQ_BF16, ld_y,
+                                     (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// internal.hpp -- launchers shared between the C ABI layer and the kernel sources.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Rowwise quantize: line l = row l of src, K = cols.  flat: the whole problem is one
+// dense run of blocks (ld_src == K == Kp, ld_codes == Kp, ld_scales == nb).
+// vec: every 8-element chunk of src can be read with 16-byte loads.
+hipError_t launch_quant_rows(const void* src, int src_bf16, int64_t rows, int64_t K, int64_t ld_src,
+                             int fmt, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                             int64_t ld_scales, bool flat, bool vec, hipStream_t stream);
+
+// Columnwise quantize: line l = column l of src [rows][ld_src], K = rows, codes and
+// scales stored [cols][ld].
+hipError_t launch_quant_cols(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src,
+                             int fmt, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                             int64_t ld_scales, bool vec, hipStream_t stream);
+
+hipError_t launch_dequant(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales, int64_t ld_scales,
+                          int fmt, int64_t L, int64_t K, void* dst, int dst_bf16, int64_t ld_dst,
+                          bool vec, hipStream_t stream);
+
+hipError_t launch_gemm(int64_t M, int64_t N, int64_t K,
+                       const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_fmt,
+                       const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws, int w_fmt,
+                       float alpha, const float* bias, void* y, int y_bf16, int64_t ld_y, hipStream_t stream);
+
+}  // namespace mxq

@@ -1,0 +1,360 @@
+// quantize.hip -- MX block quantization (mx_quantize) for gfx950.
+//
+// "Low-Precision GPU Programming", "Microscaling: the two-row experiment": per 32-element
+// block along K take amax, choose the power-of-two scale S = 2^e that rounds amax/fmax
+// upward (e >= -127; zero block -> S = 1), store e + 127 as the E8M0 byte and the codes
+// RNE(x / S).  "Scale ownership and the GEMM dataflow": a partial final block is
+// zero-padded.  "Scaling architectures" / "Current scaling": the amax reduction and the
+// dependent cast stay on the device -- here in one pass over the data, since the MX amax
+// is local to a block of 32 values.
+//
+// Encoding: v_cvt_scalef32_pk_{fp8,bf8}_{bf16,f32} computes RNE(x / scale) for a
+// power-of-two fp32 scale; it is used for every block whose scale byte is 1..254 (the
+// scale rule keeps |x / S| <= fmax, so its non-saturating overflow behaviour is never
+// reached).  Scale byte 0 (S = 2^-127, not a normal fp32) takes the software encoder.
+#include <type_traits>
+
+#include "codec.hpp"
+#include "internal.hpp"
+
+namespace mxq {
+namespace {
+
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+
+// Max over 32-bit patterns of the four lanes of a quad (quad_perm DPP: 1,0,3,2 then 2,3,0,1).
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  v = v > o ? v : o;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  return v > o ? v : o;
+}
+
+__device__ __forceinline__ uint32_t pk_abs_max_bf16(uint32_t acc, uint32_t w) {
+  v2u16 a = __builtin_bit_cast(v2u16, acc);
+  v2u16 b = __builtin_bit_cast(v2u16, w & 0x7FFF7FFFu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+
+// Encode two bf16 values (packed in one dword, element 0 in the low half) with the
+// hardware scaled conversion; result bytes in the low 16 bits (hi = false) or high.
+template <int F>
+__device__ __forceinline__ uint32_t cvt2_bf16(uint32_t old, uint32_t w, float scale, bool hi) {
+  v2s o = __builtin_bit_cast(v2s, old);
+  v2bf x = __builtin_bit_cast(v2bf, w);
+  v2s r;
+  if (hi) {
+    if (F == kE4M3) r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, x, scale, true);
+    else r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(o, x, scale, true);
+  } else {
+    if (F == kE4M3) r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, x, scale, false);
+    else r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(o, x, scale, false);
+  }
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int F>
+__device__ __forceinline__ uint32_t cvt2_f32(uint32_t old, uint32_t a, uint32_t b, float scale, bool hi) {
+  v2s o = __builtin_bit_cast(v2s, old);
+  v2s r;
+  if (hi) {
+    if (F == kE4M3) r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, __uint_as_float(a), __uint_as_float(b), scale, true);
+    else r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(o, __uint_as_float(a), __uint_as_float(b), scale, true);
+  } else {
+    if (F == kE4M3) r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, __uint_as_float(a), __uint_as_float(b), scale, false);
+    else r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(o, __uint_as_float(a), __uint_as_float(b), scale, false);
+  }
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// 8 source values of one chunk, kept as they were loaded:
+//   bf16: 4 dwords, two values each (element 2i low, 2i+1 high); f32: 8 dwords.
+template <int SRC_BF16> struct Chunk;
+template <> struct Chunk<1> { uint32_t w[4]; };
+template <> struct Chunk<0> { uint32_t w[8]; };
+
+template <int SRC_BF16>
+__device__ __forceinline__ uint32_t value_bits(const Chunk<SRC_BF16>& c, int i) {
+  if (SRC_BF16) return (i & 1) ? (c.w[i >> 1] & 0xFFFF0000u) : (c.w[i >> 1] << 16);
+  return c.w[i];
+}
+
+// Codes of the 8 values of a chunk under scale byte sb (1..254: hardware conversion;
+// 0: software RNE after multiplying by 2^127, exact for such tiny blocks; 255: NaN
+// block, all 0x7F).  Returns 8 code bytes in two dwords.
+template <int SRC_BF16, int F>
+__device__ __forceinline__ void encode_chunk(const Chunk<SRC_BF16>& c, uint32_t sb, uint32_t& d0, uint32_t& d1) {
+  if (sb == 255u) {
+    d0 = d1 = 0x7F7F7F7Fu;
+    return;
+  }
+  if (sb == 0u) {
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) b[i] = encode_rne_sat<F>(__uint_as_float(value_bits<SRC_BF16>(c, i)) * 0x1p127f);
+    d0 = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+    d1 = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    return;
+  }
+  const float scale = __uint_as_float(sb << 23);  // 2^(sb-127)
+  if (SRC_BF16) {
+    d0 = cvt2_bf16<F>(0u, c.w[0], scale, false);
+    d0 = cvt2_bf16<F>(d0, c.w[1], scale, true);
+    d1 = cvt2_bf16<F>(0u, c.w[2], scale, false);
+    d1 = cvt2_bf16<F>(d1, c.w[3], scale, true);
+  } else {
+    d0 = cvt2_f32<F>(0u, c.w[0], c.w[1], scale, false);
+    d0 = cvt2_f32<F>(d0, c.w[2], c.w[3], scale, true);
+    d1 = cvt2_f32<F>(0u, c.w[4], c.w[5], scale, false);
+    d1 = cvt2_f32<F>(d1, c.w[6], c.w[7], scale, true);
+  }
+}
+
+template <int SRC_BF16>
+__device__ __forceinline__ uint32_t chunk_abs_max(const Chunk<SRC_BF16>& c) {
+  if (SRC_BF16) {
+    uint32_t m = pk_abs_max_bf16(0u, c.w[0]);
+    m = pk_abs_max_bf16(m, c.w[1]);
+    m = pk_abs_max_bf16(m, c.w[2]);
+    m = pk_abs_max_bf16(m, c.w[3]);
+    uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+    return (lo > hi ? lo : hi) << 16;
+  } else {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t a = c.w[i] & 0x7FFFFFFFu;
+      m = m > a ? m : a;
+    }
+    return m;
+  }
+}
+
+// Load chunk: elements k0 .. k0+7 of a line starting at `line` (element pointer).
+template <int SRC_BF16, bool VEC>
+__device__ __forceinline__ void load_chunk(Chunk<SRC_BF16>& c, const void* line, int64_t k0, int64_t K) {
+  if (VEC) {
+    if (k0 < K) {
+      if (SRC_BF16) {
+        uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(line) + k0);
+        c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
+      } else {
+        const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(line) + k0);
+        uint4 v0 = p[0], v1 = p[1];
+        c.w[0] = v0.x; c.w[1] = v0.y; c.w[2] = v0.z; c.w[3] = v0.w;
+        c.w[4] = v1.x; c.w[5] = v1.y; c.w[6] = v1.z; c.w[7] = v1.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < (SRC_BF16 ? 4 : 8); ++i) c.w[i] = 0u;
+    }
+  } else {
+    if (SRC_BF16) {
+      const uint16_t* p = reinterpret_cast<const uint16_t*>(line);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t lo = (k0 + 2 * i < K) ? p[k0 + 2 * i] : 0u;
+        uint32_t hi = (k0 + 2 * i + 1 < K) ? p[k0 + 2 * i + 1] : 0u;
+        c.w[i] = lo | (hi << 16);
+      }
+    } else {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(line);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c.w[i] = (k0 + i < K) ? p[k0 + i] : 0u;
+    }
+  }
+}
+
+// One quad (4 lanes) per 32-element block, 8 consecutive elements per lane.  Blocks are
+// numbered g = row * nb + b; FLAT problems are one dense run so row = 0, b = g.  Each
+// thread keeps U blocks in flight (loads first, then reduce + encode + store).
+template <int SRC_BF16, int F, bool FLAT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_quant_rows(const void* __restrict__ src, int64_t ld_src, int64_t K,
+                                                        int64_t nb, int64_t nblocks, uint8_t* __restrict__ codes,
+                                                        int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales) {
+  constexpr int U = 4;
+  constexpr int ES = SRC_BF16 ? 2 : 4;
+  const int q = threadIdx.x & 3;
+  const int64_t stride = (int64_t)gridDim.x * (kThreads / 4);
+  for (int64_t g0 = (int64_t)blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2); g0 < nblocks; g0 += stride * U) {
+    Chunk<SRC_BF16> c[U];
+    int64_t row[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t g = g0 + u * stride;
+      if (FLAT) { row[u] = 0; b[u] = g; }
+      else { row[u] = g / nb; b[u] = g - row[u] * nb; }
+      if (g < nblocks) {
+        const char* line = reinterpret_cast<const char*>(src) + row[u] * ld_src * ES;
+        // a flat problem has no partial chunks: every chunk index is in range
+        load_chunk<SRC_BF16, VEC>(c[u], line, 32 * b[u] + 8 * q, FLAT ? (int64_t)INT64_MAX : K);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t g = g0 + u * stride;
+      if (g < nblocks) {
+        uint32_t amax = quad_max(chunk_abs_max<SRC_BF16>(c[u]));
+        uint32_t sb = scale_byte_from_amax<F>(amax);
+        uint32_t d0, d1;
+        encode_chunk<SRC_BF16, F>(c[u], sb, d0, d1);
+        *reinterpret_cast<uint2*>(codes + row[u] * ld_codes + 32 * b[u] + 8 * q) = make_uint2(d0, d1);
+        if (q == 0) scales[row[u] * ld_scales + b[u]] = (uint8_t)sb;
+      }
+    }
+  }
+}
+
+// Columnwise: a workgroup stages a tile of 128 rows (4 blocks of K) x 64 columns in LDS,
+// then thread (c = tid % 64, kb = tid / 64) reduces and encodes the 32 values of block kb
+// of column c and writes its 32 codes (K-contiguous in the transposed output).
+constexpr int kColTileRows = 128;
+constexpr int kColTileCols = 64;
+
+template <int SRC_BF16, int F, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_quant_cols(const void* __restrict__ src, int64_t rows, int64_t cols,
+                                                        int64_t ld_src, int64_t nb, uint8_t* __restrict__ codes,
+                                                        int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales) {
+  typedef typename std::conditional<SRC_BF16, uint16_t, uint32_t>::type E;
+  __shared__ E tile[kColTileRows][kColTileCols];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kColTileCols;
+  const E* s = reinterpret_cast<const E*>(src);
+  for (int64_t ty = blockIdx.y; ty * kColTileRows < rows; ty += gridDim.y) {
+    const int64_t r0 = ty * kColTileRows;
+    // stage: 16-byte pieces of each tile row
+    constexpr int EPV = 16 / sizeof(E);                 // elements per 16-byte piece
+    constexpr int PPR = kColTileCols / EPV;             // pieces per tile row
+    for (int p = tid; p < kColTileRows * PPR; p += kThreads) {
+      int tr = p / PPR, tc = (p % PPR) * EPV;
+      int64_t r = r0 + tr, cc = c0 + tc;
+      E* dst = &tile[tr][tc];
+      if (VEC && r < rows && cc + EPV <= cols) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(s + r * ld_src + cc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) dst[i] = (r < rows && cc + i < cols) ? s[r * ld_src + cc + i] : (E)0;
+      }
+    }
+    __syncthreads();
+    const int c = tid % kColTileCols, kb = tid / kColTileCols;
+    const int64_t col = c0 + c, b = r0 / 32 + kb;
+    if (col < cols && b < nb) {
+      uint32_t amax = 0;
+      uint32_t v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        uint32_t x = tile[32 * kb + i][c];
+        v[i] = SRC_BF16 ? (x << 16) : x;
+        uint32_t a = v[i] & 0x7FFFFFFFu;
+        amax = amax > a ? amax : a;
+      }
+      uint32_t sb = scale_byte_from_amax<F>(amax);
+      uint32_t out[8];
+      if (sb == 255u) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = 0x7F7F7F7Fu;
+      } else if (sb == 0u) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w |= encode_rne_sat<F>(__uint_as_float(v[4 * i + j]) * 0x1p127f) << (8 * j);
+          out[i] = w;
+        }
+      } else {
+        const float scale = __uint_as_float(sb << 23);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t w = cvt2_f32<F>(0u, v[4 * i], v[4 * i + 1], scale, false);
+          out[i] = cvt2_f32<F>(w, v[4 * i + 2], v[4 * i + 3], scale, true);
+        }
+      }
+      uint4* dst = reinterpret_cast<uint4*>(codes + col * ld_codes + 32 * b);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      scales[col * ld_scales + b] = (uint8_t)sb;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+template <int SRC_BF16, int F>
+static hipError_t quant_rows_t(const void* src, int64_t rows, int64_t K, int64_t ld_src, uint8_t* codes,
+                               int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool flat, bool vec,
+                               hipStream_t stream) {
+  const int64_t nb = (K + 31) / 32;
+  const int64_t nblocks = rows * nb;
+  const int64_t wg_needed = (nblocks + 63) / 64;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int grid = (int)(wg_needed < cap ? wg_needed : cap);
+  if (flat && vec)
+    hipLaunchKernelGGL((k_quant_rows<SRC_BF16, F, true, true>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src, K,
+                       nb, nblocks, codes, ld_codes, scales, ld_scales);
+  else if (vec)
+    hipLaunchKernelGGL((k_quant_rows<SRC_BF16, F, false, true>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src, K,
+                       nb, nblocks, codes, ld_codes, scales, ld_scales);
+  else
+    hipLaunchKernelGGL((k_quant_rows<SRC_BF16, F, false, false>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src,
+                       K, nb, nblocks, codes, ld_codes, scales, ld_scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const void* src, int src_bf16, int64_t rows, int64_t K, int64_t ld_src, int fmt,
+                             uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool flat,
+                             bool vec, hipStream_t stream) {
+  if (src_bf16) {
+    if (fmt == kE4M3) return quant_rows_t<1, kE4M3>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
+    return quant_rows_t<1, kE5M2>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
+  }
+  if (fmt == kE4M3) return quant_rows_t<0, kE4M3>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
+  return quant_rows_t<0, kE5M2>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
+}
+
+template <int SRC_BF16, int F>
+static hipError_t quant_cols_t(const void* src, int64_t rows, int64_t cols, int64_t ld_src, uint8_t* codes,
+                               int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec, hipStream_t stream) {
+  const int64_t nb = (rows + 31) / 32;
+  const int64_t gx = (cols + kColTileCols - 1) / kColTileCols;
+  int64_t gy = (rows + kColTileRows - 1) / kColTileRows;
+  if (gy > 65535) gy = 65535;
+  if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (vec)
+    hipLaunchKernelGGL((k_quant_cols<SRC_BF16, F, true>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream,
+                       src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales);
+  else
+    hipLaunchKernelGGL((k_quant_cols<SRC_BF16, F, false>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream,
+                       src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_cols(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, int fmt,
+                             uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec,
+                             hipStream_t stream) {
+  if (src_bf16) {
+    if (fmt == kE4M3) return quant_cols_t<1, kE4M3>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+    return quant_cols_t<1, kE5M2>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+  }
+  if (fmt == kE4M3) return quant_cols_t<0, kE4M3>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+  return quant_cols_t<0, kE5M2>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+}
+
+}  // namespace mxq

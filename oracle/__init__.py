@@ -61,6 +61,8 @@ def lib():
         L.mxo_scale_byte.argtypes = [ctypes.c_double, ctypes.c_int]
         L.mxo_num_finite_codes.restype = ctypes.c_int
         L.mxo_num_finite_codes.argtypes = [ctypes.c_int]
+        L.mxo_num_threads.restype = ctypes.c_int
+        L.mxo_num_threads.argtypes = []
         L.mxo_round_bf16.restype = ctypes.c_uint16
         L.mxo_round_bf16.argtypes = [ctypes.c_double]
         L.mxo_quantize.restype = None
@@ -110,6 +112,11 @@ def scale_byte(amax: float, fmt: str) -> int:
 
 def num_finite_codes(fmt: str) -> int:
     return int(lib().mxo_num_finite_codes(FMT[fmt]))
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().mxo_num_threads())
 
 
 def round_bf16(v: float) -> int:

