@@ -70,6 +70,30 @@ typedef enum {
 } mxq_axis;
 
 /*
+ * Accumulation contract of mxq_gemm ("Accumulator type isn't the whole arithmetic
+ * contract": a declared FP32 accumulator can hide reduced internal precision, so the
+ * mode is an explicit argument).  Both modes accumulate in FP32 across the K loop.
+ *
+ * MXQ_ACC_FP8_MFMA  the block-scaled FP8 matrix-core instruction
+ *                   (v_mfma_scale_f32_32x32x64_f8f6f4) consumes codes and E8M0 scales
+ *                   directly.  Measured behaviour on gfx950: every product is exact, but
+ *                   inside each group of 8 consecutive k of a block the products are
+ *                   aligned to the group's largest one and truncated toward zero about 13
+ *                   bits below it before the group sum; group sums, scales and the
+ *                   accumulator then combine in FP32.  Error per output element
+ *                   <= sum over groups g of 7 * 2^-12 * S_g * max_{k in g} |binade
+ *                   products| + FP32 summation error.  Full MXFP8 matrix-core rate.
+ * MXQ_ACC_FP32      every scaled product is formed exactly and summed in FP32: codes are
+ *                   decoded with their block scale to bf16 in registers (exact while
+ *                   each 2^(s-127) * code lies inside bf16's range, i.e. for scale
+ *                   bytes roughly 10..245) and fed to v_mfma_f32_32x32x16_bf16, whose
+ *                   products are exact and sums FP32.  Meets |y - y_exact| <= 1e-5 *
+ *                   sum_k |scaled products| for ordinary data.  Half the FP8 matrix-core
+ *                   rate at best.
+ */
+typedef enum { MXQ_ACC_FP8_MFMA = 0, MXQ_ACC_FP32 = 1 } mxq_accum;
+
+/*
  * mxq_quantize -- MX block quantization of a 2-D bf16/fp32 matrix.
  *
  * src      [rows][ld_src] row-major, src_type MXQ_F32 or MXQ_BF16, ld_src >= cols.
@@ -119,21 +143,21 @@ int mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales
  *          ld_xs, ld_ws >= nb.
  * Result   acc[i][j] = sum_b 2^(sx[i][b] + sw[j][b] - 254) * sum_{k in b, k < K}
  *                        dec(x[i][k]) * dec(w[j][k])
- *          accumulated in FP32 (the products and the per-block scaling are done by the
- *          matrix cores; summation order is implementation-defined); code positions
- *          k >= K are ignored.  Epilogue: y = alpha * acc (+ bias[j] if bias != NULL),
- *          rounded once to y_type.
+ *          accumulated as `accum` states (see mxq_accum; summation order is
+ *          implementation-defined); code positions k >= K and scale bytes of blocks
+ *          >= nb are ignored.  Epilogue: y = alpha * acc (+ bias[j] if bias != NULL, one
+ *          FP32 fma), rounded once to y_type.
  * bias     [N] FP32 device array or NULL.
  * y        [M][ld_y] row-major, y_type MXQ_F32 or MXQ_BF16 (RNE), ld_y >= N, pointer
  *          aligned to its element size.
  * alpha    must be finite.
- * Accuracy: |y - y_exact| <= 1e-5 * |alpha| * sum_k |scaled products| (plus one rounding
- * of the bias add and of the output cast).
+ * accum    MXQ_ACC_FP8_MFMA (fast) or MXQ_ACC_FP32 (exact products), see mxq_accum.
+ * Limits   M, N < 2^31, K < 2^24, ld_x and ld_w < 2^24, ld_xs and ld_ws < 2^23.
  */
 int mxq_gemm(int64_t M, int64_t N, int64_t K,
              const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_elem,
              const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws, int w_elem,
-             float alpha, const float* bias, void* y, int y_type, int64_t ld_y, void* stream);
+             float alpha, const float* bias, void* y, int y_type, int64_t ld_y, int accum, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* mxq_status_string(int status);

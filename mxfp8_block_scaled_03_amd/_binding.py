@@ -9,8 +9,10 @@ _LIB_PATH = os.path.join(PKG, "libmxq.so")
 
 MXQ_F32, MXQ_BF16, MXQ_E4M3, MXQ_E5M2 = 0, 1, 2, 3
 MXQ_ROWWISE, MXQ_COLWISE = 0, 1
+MXQ_ACC_FP8_MFMA, MXQ_ACC_FP32 = 0, 1
 
 _ELEM = {"e4m3": MXQ_E4M3, "e5m2": MXQ_E5M2}
+_ACC = {"fp8": MXQ_ACC_FP8_MFMA, "fp32": MXQ_ACC_FP32}
 _AXIS = {"row": MXQ_ROWWISE, "col": MXQ_COLWISE, 0: MXQ_ROWWISE, 1: MXQ_COLWISE}
 
 
@@ -44,7 +46,7 @@ def lib():
         L.mxq_dequantize.argtypes = [vp, i64, vp, i64, ci, i64, i64, vp, ci, i64, vp]
         L.mxq_gemm.restype = ci
         L.mxq_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, ci, vp, i64, vp, i64, ci,
-                               ctypes.c_float, vp, vp, ci, i64, vp]
+                               ctypes.c_float, vp, vp, ci, i64, ci, vp]
         L.mxq_status_string.restype = ctypes.c_char_p
         L.mxq_status_string.argtypes = [ci]
         L.mxq_version.restype = ci
@@ -66,9 +68,9 @@ def mxq_dequantize(codes, ld_codes, scales, ld_scales, elem, L, K, dst, dst_type
 
 
 def mxq_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws, w_elem,
-             alpha, bias, y, y_type, ld_y, stream=None) -> int:
+             alpha, bias, y, y_type, ld_y, accum=MXQ_ACC_FP8_MFMA, stream=None) -> int:
     return lib().mxq_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws,
-                          w_elem, alpha, bias, y, y_type, ld_y, stream)
+                          w_elem, alpha, bias, y, y_type, ld_y, accum, stream)
 
 
 def mxq_status_string(status: int) -> str:
@@ -151,9 +153,10 @@ def dequantize(codes, scales, K: int, elem: str = "e4m3", out_dtype=None):
 
 
 def gemm(x_codes, x_scales, w_codes, w_scales, K: int, x_elem: str = "e4m3", w_elem: str = "e4m3",
-         alpha: float = 1.0, bias=None, out_dtype=None, out=None):
+         alpha: float = 1.0, bias=None, out_dtype=None, out=None, accum: str = "fp8"):
     """Y[M][N] = alpha * (X W) + bias with X = (x_codes [M][Kp], x_scales) and W column-major
-    (w_codes [N][Kp], w_scales)."""
+    (w_codes [N][Kp], w_scales).  accum="fp8": FP8 matrix cores (fast); accum="fp32":
+    exact products summed in FP32 (see mxq_accum in include/mxq.h)."""
     torch = _torch()
     M, N = x_codes.shape[0], w_codes.shape[0]
     if out is None:
@@ -163,6 +166,6 @@ def gemm(x_codes, x_scales, w_codes, w_scales, K: int, x_elem: str = "e4m3", w_e
     st = mxq_gemm(M, N, K, x_codes.data_ptr(), x_codes.stride(0), x_scales.data_ptr(), x_scales.stride(0),
                   _ELEM[x_elem], w_codes.data_ptr(), w_codes.stride(0), w_scales.data_ptr(), w_scales.stride(0),
                   _ELEM[w_elem], float(alpha), None if bias is None else bias.data_ptr(), out.data_ptr(),
-                  _wide_type(out), out.stride(0), _stream_handle())
+                  _wide_type(out), out.stride(0), _ACC[accum], _stream_handle())
     _check(st, "mxq_gemm")
     return out

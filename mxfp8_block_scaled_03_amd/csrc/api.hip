@@ -88,8 +88,9 @@ int mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales
 
 int mxq_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales,
              int64_t ld_xs, int x_elem, const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws,
-             int w_elem, float alpha, const float* bias, void* y, int y_type, int64_t ld_y, void* stream) {
+             int w_elem, float alpha, const float* bias, void* y, int y_type, int64_t ld_y, int accum, void* stream) {
   if (!is_elem(x_elem) || !is_elem(w_elem) || !is_wide(y_type)) return MXQ_ERR_DTYPE;
+  if (accum != MXQ_ACC_FP8_MFMA && accum != MXQ_ACC_FP32) return MXQ_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxCodeLd) return MXQ_ERR_SHAPE;
   if (!isfinite(alpha)) return MXQ_ERR_ARG;
   if (M == 0 || N == 0) return MXQ_OK;
@@ -109,7 +110,7 @@ int mxq_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld
   if (!aligned(y, (uintptr_t)ey) || (bias && !aligned(bias, 4))) return MXQ_ERR_ALIGN;
   return hip_status(mxq::launch_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, to_fmt(x_elem), w_codes, ld_w, w_scales,
                                      ld_ws, to_fmt(w_elem), alpha, bias, y, y_type == MXQ_BF16, ld_y,
-                                     (hipStream_t)stream));
+                                     accum == MXQ_ACC_FP32, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -35,6 +35,8 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int BM = 256, BN = 256, BK = 128;
@@ -116,6 +118,82 @@ __device__ __forceinline__ void compute_step(const FragAddr& fa, uint32_t so, co
   }
 }
 
+// The four E8M0 bytes of K step t (blocks 4t..4t+3) of one row, byte b = block 4t+b;
+// blocks past the end read as 127.
+__device__ __forceinline__ uint32_t load_scale_quad(const uint8_t* rowp, int t, int nb) {
+  uint32_t q = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int blk = 4 * t + b;
+    uint32_t v = rowp[min(blk, nb - 1)];
+    q |= (blk < nb ? v : 127u) << (8 * b);
+  }
+  return q;
+}
+
+// fp32 value 2^(byte-127) of an E8M0 byte (byte 0 is the fp32 subnormal 2^-127; 255 NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t byte) {
+  return __uint_as_float(byte == 0 ? 0x00400000u : (byte == 255 ? 0x7FC00000u : byte << 23));
+}
+
+// Eight codes (two dwords) -> eight bf16 values code * scale (exact while the product is
+// inside bf16's range), with the gfx950 scaled conversion.
+template <int F>
+__device__ __forceinline__ v8bf codes_to_bf16(uint32_t w0, uint32_t w1, float s) {
+  v2bf p0, p1, p2, p3;
+  if (F == kE4M3) {
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true);
+  } else {
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, s, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, s, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, s, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, s, true);
+  }
+  typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+  v4bf lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  v4bf hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Exact-product accumulation: each lane decodes its codes with their block scale into
+// bf16 (exact) and feeds v_mfma_f32_32x32x16_bf16, whose products are exact and whose
+// sums are FP32.  Per 32-wide block, lane (i, g) holds k = 16g..16g+15 of the block:
+// bytes 0..7 go to the first 16-wide MFMA, bytes 8..15 to the second (A and B lanes
+// use the same assignment, so each MFMA contracts a matching set of 16 k).
+template <int FA, int FB>
+__device__ __forceinline__ void compute_step_exact(const FragAddr& fa, uint32_t so, const uint32_t (&sqa)[4],
+                                                   const uint32_t (&sqb)[4], v16f (&acc)[4][4]) {
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    v4i ra[4], rb[4];
+    float sa[4], sb[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      ra[f] = lds16(fa.a[blk >> 1][blk & 1] + so, 4096 * f);
+      rb[f] = lds16(fa.b[blk >> 1][blk & 1] + so, 4096 * f);
+      sa[f] = e8m0_to_f32((sqa[f] >> (8 * blk)) & 0xFFu);
+      sb[f] = e8m0_to_f32((sqb[f] >> (8 * blk)) & 0xFFu);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v8bf a[4], b[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        a[f] = codes_to_bf16<FA>((uint32_t)ra[f][2 * h], (uint32_t)ra[f][2 * h + 1], sa[f]);
+        b[f] = codes_to_bf16<FB>((uint32_t)rb[f][2 * h], (uint32_t)rb[f][2 * h + 1], sb[f]);
+      }
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < 4; ++fj)
+          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fi], b[fj], acc[fi][fj], 0, 0, 0);
+    }
+  }
+}
+
 // Zero the code bytes at k >= krem of every row of both tiles of one stage (the last,
 // partial K step), in place in LDS.  Thread t owns tile row t of A and of B.
 __device__ __forceinline__ void mask_tail(uint32_t so, int krem) {
@@ -135,7 +213,7 @@ __device__ __forceinline__ void mask_tail(uint32_t so, int krem) {
   }
 }
 
-template <int FA, int FB, int Y_BF16, bool BIAS>
+template <int MODE, int FA, int FB, int Y_BF16, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(int M, int N, int K, int tiles_m, int tiles_n,
                                                      const uint8_t* __restrict__ xc, int64_t ld_x,
                                                      const uint8_t* __restrict__ xs, int64_t ld_xs,
@@ -230,13 +308,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(int M, int N, int K, int t
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // scale operands of the current step: MODE 0 holds blocks (4t+g, 4t+2+g) for the
+  // scaled MFMA, MODE 1 the four bytes of the step
+  auto scales_of = [&](const uint8_t* rowp, int t_) {
+    return MODE == 0 ? load_scale_pair(rowp, t_, lg, nb) : load_scale_quad(rowp, t_, nb);
+  };
   uint32_t sa[4], sb[4];
   if (nsteps > 0) {
     issue(0, 0);
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      sa[f] = load_scale_pair(xs_tile + xs_off[f], 0, lg, nb);
-      sb[f] = load_scale_pair(ws_tile + ws_off[f], 0, lg, nb);
+      sa[f] = scales_of(xs_tile + xs_off[f], 0);
+      sb[f] = scales_of(ws_tile + ws_off[f], 0);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -250,14 +333,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(int M, int N, int K, int t
     uint32_t na[4], nbx[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      na[f] = load_scale_pair(xs_tile + xs_off[f], tn_, lg, nb);
-      nbx[f] = load_scale_pair(ws_tile + ws_off[f], tn_, lg, nb);
+      na[f] = scales_of(xs_tile + xs_off[f], tn_);
+      nbx[f] = scales_of(ws_tile + ws_off[f], tn_);
     }
     if (tail && s == nsteps - 1) {
       mask_tail(so, krem_last);
       __syncthreads();
     }
-    compute_step<FA, FB>(fa, so, sa, sb, acc);
+    if (MODE == 0)
+      compute_step<FA, FB>(fa, so, sa, sb, acc);
+    else
+      compute_step_exact<FA, FB>(fa, so, sa, sb, acc);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
@@ -286,12 +372,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(int M, int N, int K, int t
   }
 }
 
-template <int FA, int FB, int Y_BF16, bool BIAS>
+template <int MODE, int FA, int FB, int Y_BF16, bool BIAS>
 hipError_t gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
                   const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, float alpha, const float* bias,
                   void* y, int64_t ld_y, hipStream_t stream) {
   static bool attr_set[64] = {false};
-  auto kern = k_gemm<FA, FB, Y_BF16, BIAS>;
+  auto kern = k_gemm<MODE, FA, FB, Y_BF16, BIAS>;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (!attr_set[dev]) {
@@ -306,31 +392,40 @@ hipError_t gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld
   return hipGetLastError();
 }
 
-template <int FA, int FB>
+template <int MODE, int FA, int FB>
 hipError_t gemm_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
                   const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, float alpha, const float* bias,
                   void* y, int y_bf16, int64_t ld_y, hipStream_t stream) {
   if (y_bf16) {
-    if (bias) return gemm_t<FA, FB, 1, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
-    return gemm_t<FA, FB, 1, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
+    if (bias) return gemm_t<MODE, FA, FB, 1, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
+    return gemm_t<MODE, FA, FB, 1, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
   }
-  if (bias) return gemm_t<FA, FB, 0, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
-  return gemm_t<FA, FB, 0, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
+  if (bias) return gemm_t<MODE, FA, FB, 0, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
+  return gemm_t<MODE, FA, FB, 0, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
+}
+
+template <int MODE>
+hipError_t gemm_m(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
+                  int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, int w_fmt, float alpha,
+                  const float* bias, void* y, int y_bf16, int64_t ld_y, hipStream_t stream) {
+  if (x_fmt == kE4M3 && w_fmt == kE4M3)
+    return gemm_f<MODE, 0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
+  if (x_fmt == kE4M3)
+    return gemm_f<MODE, 0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
+  if (w_fmt == kE4M3)
+    return gemm_f<MODE, 1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
+  return gemm_f<MODE, 1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
                        int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
-                       int w_fmt, float alpha, const float* bias, void* y, int y_bf16, int64_t ld_y,
+                       int w_fmt, float alpha, const float* bias, void* y, int y_bf16, int64_t ld_y, int exact,
                        hipStream_t stream) {
-  if (x_fmt == kE4M3 && w_fmt == kE4M3)
-    return gemm_f<0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
-  if (x_fmt == kE4M3)
-    return gemm_f<0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
-  if (w_fmt == kE4M3)
-    return gemm_f<1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
-  return gemm_f<1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
+  if (exact)
+    return gemm_m<1>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, alpha, bias, y, y_bf16, ld_y, stream);
+  return gemm_m<0>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, alpha, bias, y, y_bf16, ld_y, stream);
 }
 
 }  // namespace mxq

@@ -28,6 +28,7 @@ hipError_t launch_dequant(const uint8_t* codes, int64_t ld_codes, const uint8_t*
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K,
                        const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_fmt,
                        const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws, int w_fmt,
-                       float alpha, const float* bias, void* y, int y_bf16, int64_t ld_y, hipStream_t stream);
+                       float alpha, const float* bias, void* y, int y_bf16, int64_t ld_y, int exact,
+                       hipStream_t stream);
 
 }  // namespace mxq

@@ -71,11 +71,11 @@ def test_quantize_validation():
 
 def g(**kw):
     a = dict(M=8, N=8, K=64, xc=FAKE, ld_x=64, xs=FAKE, ld_xs=2, xe=mxq.MXQ_E4M3, wc=FAKE, ld_w=64, ws=FAKE,
-             ld_ws=2, we=mxq.MXQ_E4M3, alpha=1.0, bias=None, y=FAKE, yt=mxq.MXQ_F32, ld_y=8)
+             ld_ws=2, we=mxq.MXQ_E4M3, alpha=1.0, bias=None, y=FAKE, yt=mxq.MXQ_F32, ld_y=8, acc=0)
     a.update(kw)
     return mxq.mxq_gemm(a["M"], a["N"], a["K"], a["xc"], a["ld_x"], a["xs"], a["ld_xs"], a["xe"], a["wc"],
                         a["ld_w"], a["ws"], a["ld_ws"], a["we"], a["alpha"], a["bias"], a["y"], a["yt"], a["ld_y"],
-                        None)
+                        a["acc"], None)
 
 
 def test_gemm_validation():
@@ -85,11 +85,14 @@ def test_gemm_validation():
     assert g(K=1 << 24) == -2
     assert g(alpha=float("nan")) == -6
     assert g(alpha=float("inf")) == -6
+    assert g(acc=2) == -6
+    assert g(acc=-1) == -6
     assert g(y=None) == -1
     assert g(xc=None) == -1
     assert g(ws=None) == -1
     assert g(ld_x=32) == -3
     assert g(ld_ws=1) == -3
+    assert g(ld_xs=1 << 23) == -3
     assert g(ld_y=7) == -3
     assert g(ld_x=72) == -4
     assert g(wc=FAKE + 4) == -4

@@ -1,7 +1,10 @@
 """GPU parity of mxq_gemm against the FP64 oracle evaluated on the GPU's own codes and
-scales.  Every compared element must satisfy the matrix-core contract bound and the
-fraction within the strict 1e-5 * sum_k |S_X S_W Xq Wq| bound is reported (see
-gpu_helpers for both bounds)."""
+scales, in both accumulation modes:
+  accum="fp32" (exact products, FP32 sums): every element within the strict bound
+               |y - y_ref| <= 1e-5 * sum_k |S_X S_W Xq Wq| (+ epilogue roundings);
+  accum="fp8"  (FP8 matrix cores): every element within the measured matrix-core
+               contract bound; the fraction within the strict bound is reported.
+See gpu_helpers for both bounds."""
 import numpy as np
 import pytest
 import torch
@@ -20,38 +23,45 @@ def quantized(rng, rows, K, std, fmt):
     return mxq.quantize(x, fmt, "row")
 
 
+ACCS = ["fp8", "fp32"]
+
+
 def run_case(M, N, K, fx="e4m3", fw="e4m3", out=torch.float32, alpha=1.0, bias=False, seed=0, xstd=1.0,
-             what=""):
+             what="", accum="fp8"):
     rng = np.random.default_rng(seed)
     xc, xs = quantized(rng, M, max(K, 1), xstd, fx)
     wc, ws = quantized(rng, N, max(K, 1), 0.02, fw)
     b = torch.from_numpy(rng.standard_normal(N).astype(np.float32) * 0.02).to(DEV) if bias else None
-    y = mxq.gemm(xc, xs, wc, ws, K, fx, fw, alpha=alpha, bias=b, out_dtype=out)
+    y = mxq.gemm(xc, xs, wc, ws, K, fx, fw, alpha=alpha, bias=b, out_dtype=out, accum=accum)
     torch.cuda.synchronize()
-    return full_check(xc, xs, fx, wc, ws, fw, K, y, out, alpha=alpha, bias=b, what=what)
+    return full_check(xc, xs, fx, wc, ws, fw, K, y, out, alpha=alpha, bias=b, what="%s %s" % (accum, what),
+                      strict=accum == "fp32")
 
 
 SHAPES = [(1, 1, 1), (2, 1, 32), (5, 7, 33), (64, 64, 64), (300, 260, 200), (256, 256, 512), (257, 511, 128),
           (513, 257, 4001), (1, 300, 4096), (40, 30, 0)]
 
 
+@pytest.mark.parametrize("accum", ACCS)
 @pytest.mark.parametrize("M,N,K", SHAPES)
-def test_gemm_shapes_fp32(M, N, K):
-    say("gemm %dx%dx%d fp32" % (M, N, K))
-    run_case(M, N, K, what="%dx%dx%d" % (M, N, K))
+def test_gemm_shapes_fp32(M, N, K, accum):
+    say("gemm %dx%dx%d fp32 out, accum %s" % (M, N, K, accum))
+    run_case(M, N, K, what="%dx%dx%d" % (M, N, K), accum=accum)
 
 
+@pytest.mark.parametrize("accum", ACCS)
 @pytest.mark.parametrize("fx,fw", [("e5m2", "e4m3"), ("e4m3", "e5m2"), ("e5m2", "e5m2")])
-def test_gemm_formats(fx, fw):
-    say("gemm formats %s x %s" % (fx, fw))
-    run_case(300, 260, 480, fx, fw, seed=1, what="%s x %s" % (fx, fw))
+def test_gemm_formats(fx, fw, accum):
+    say("gemm formats %s x %s accum %s" % (fx, fw, accum))
+    run_case(300, 260, 480, fx, fw, seed=1, what="%s x %s" % (fx, fw), accum=accum)
 
 
+@pytest.mark.parametrize("accum", ACCS)
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("alpha,bias", [(1.0, True), (0.375, False), (-2.5, True)])
-def test_gemm_epilogue(out, alpha, bias):
-    say("gemm epilogue %s alpha=%g bias=%s" % (out, alpha, bias))
-    run_case(270, 300, 352, out=out, alpha=alpha, bias=bias, seed=2, what="epilogue")
+def test_gemm_epilogue(out, alpha, bias, accum):
+    say("gemm epilogue %s alpha=%g bias=%s accum %s" % (out, alpha, bias, accum))
+    run_case(270, 300, 352, out=out, alpha=alpha, bias=bias, seed=2, what="epilogue", accum=accum)
 
 
 def test_gemm_k_zero_writes_bias():
@@ -65,14 +75,15 @@ def test_gemm_k_zero_writes_bias():
     assert torch.equal(y, b.cpu().expand(20, 50))
 
 
-def test_gemm_ignores_bytes_past_k():
+@pytest.mark.parametrize("accum", ACCS)
+def test_gemm_ignores_bytes_past_k(accum):
     """Codes at k >= K and scale bytes of blocks >= nb are never used: garbage there (even
     NaN scale bytes) must not change Y."""
     rng = np.random.default_rng(4)
     M, N, K = 70, 90, 100           # Kp = 128, nb = 4 but only ceil(100/32) = 4 blocks
     xc, xs = quantized(rng, M, K, 1.0, "e4m3")
     wc, ws = quantized(rng, N, K, 0.02, "e4m3")
-    y0 = mxq.gemm(xc, xs, wc, ws, K, out_dtype=torch.float32)
+    y0 = mxq.gemm(xc, xs, wc, ws, K, out_dtype=torch.float32, accum=accum)
     xg = torch.full((M, 160), 0x7E, dtype=torch.uint8, device=DEV)
     wg = torch.full((N, 160), 0x7E, dtype=torch.uint8, device=DEV)
     xg[:, :K] = xc[:, :K]
@@ -81,74 +92,85 @@ def test_gemm_ignores_bytes_past_k():
     wsg = torch.full((N, 8), 255, dtype=torch.uint8, device=DEV)
     xsg[:, :4] = xs
     wsg[:, :4] = ws
-    y1 = mxq.gemm(xg, xsg, wg, wsg, K, out_dtype=torch.float32)
+    y1 = mxq.gemm(xg, xsg, wg, wsg, K, out_dtype=torch.float32, accum=accum)
     assert torch.equal(y0, y1)
 
 
-def test_gemm_two_row_fixture():
+@pytest.mark.parametrize("accum", ACCS)
+def test_gemm_two_row_fixture(accum):
     from conftest import load_golden
     g = load_golden("two_row_projection.json")
     x = torch.tensor([g["pattern_small"] * 4, g["pattern_large"] * 4], dtype=torch.float32, device=DEV)
     w_kn = torch.tensor(g["weight_pattern"] * 4, dtype=torch.float32, device=DEV).reshape(32, 1)
     xc, xs = mxq.quantize(x, "e4m3", "row")
     wc, ws = mxq.quantize(w_kn, "e4m3", "col")
-    y = mxq.gemm(xc, xs, wc, ws, 32, out_dtype=torch.float32).cpu().numpy()[:, 0]
+    y = mxq.gemm(xc, xs, wc, ws, 32, out_dtype=torch.float32, accum=accum).cpu().numpy()[:, 0]
     assert ["%.6f" % v for v in y] == ["%.6f" % v for v in g["printed"]["mxfp8_y"]]
     sel = torch.zeros((32, 1), dtype=torch.float32, device=DEV)
     sel[3, 0] = 1.0
     sc, ss = mxq.quantize(sel, "e4m3", "col")
-    ysel = mxq.gemm(xc, xs, sc, ss, 32, out_dtype=torch.float32).cpu().numpy()[:, 0]
+    ysel = mxq.gemm(xc, xs, sc, ss, 32, out_dtype=torch.float32, accum=accum).cpu().numpy()[:, 0]
     assert list(ysel) == g["selector"]["selected_mx"]
 
 
-def test_gemm_deterministic():
+@pytest.mark.parametrize("accum", ACCS)
+def test_gemm_deterministic(accum):
     rng = np.random.default_rng(5)
     xc, xs = quantized(rng, 600, 1000, 1.0, "e4m3")
     wc, ws = quantized(rng, 500, 1000, 0.02, "e4m3")
-    y0 = mxq.gemm(xc, xs, wc, ws, 1000, out_dtype=torch.float32)
+    y0 = mxq.gemm(xc, xs, wc, ws, 1000, out_dtype=torch.float32, accum=accum)
     for _ in range(3):
-        assert torch.equal(y0, mxq.gemm(xc, xs, wc, ws, 1000, out_dtype=torch.float32))
+        assert torch.equal(y0, mxq.gemm(xc, xs, wc, ws, 1000, out_dtype=torch.float32, accum=accum))
 
 
 # ----------------------------------------------------------------- full-size workloads (sampled)
 
-def test_workload2_projection():
+@pytest.mark.parametrize("accum", ACCS)
+def test_workload2_projection(accum):
     d = wl.workload2()
     xc, xs = mxq.quantize(d["x"].to(DEV), "e4m3", "row")
     wc, ws = mxq.quantize(d["w"].to(DEV), "e4m3", "row")
     for out in (torch.bfloat16, torch.float32):
-        say("workload2 gemm %s" % out)
-        y = mxq.gemm(xc, xs, wc, ws, d["K"], out_dtype=out)
-        sampled_check(xc, xs, "e4m3", wc, ws, "e4m3", d["K"], y, out, what="workload2 %s" % out)
+        say("workload2 gemm %s accum %s" % (out, accum))
+        y = mxq.gemm(xc, xs, wc, ws, d["K"], out_dtype=out, accum=accum)
+        sampled_check(xc, xs, "e4m3", wc, ws, "e4m3", d["K"], y, out, what="workload2 %s %s" % (out, accum),
+                      strict=accum == "fp32")
 
 
-def test_workload4_dgrad_wgrad():
+@pytest.mark.parametrize("accum", ACCS)
+def test_workload4_dgrad_wgrad(accum):
     d = wl.workload4()
     dyc, dys = mxq.quantize(d["dy"].to(DEV), "e5m2", "row")
     wcc, wcs = mxq.quantize(d["w"].to(DEV), "e4m3", "col")       # W^T rows: [K][N] -> contraction over N
     say("workload4 dgrad")
-    dx = mxq.gemm(dyc, dys, wcc, wcs, d["N"], "e5m2", "e4m3", out_dtype=torch.float32)
-    sampled_check(dyc, dys, "e5m2", wcc, wcs, "e4m3", d["N"], dx, torch.float32, what="dgrad")
+    dx = mxq.gemm(dyc, dys, wcc, wcs, d["N"], "e5m2", "e4m3", out_dtype=torch.float32, accum=accum)
+    sampled_check(dyc, dys, "e5m2", wcc, wcs, "e4m3", d["N"], dx, torch.float32, what="dgrad " + accum,
+                  strict=accum == "fp32")
     dyt, dyts = mxq.quantize(d["dy"].to(DEV), "e5m2", "col")     # [N][M]
     xt, xts = mxq.quantize(d["x"].to(DEV), "e4m3", "col")        # [K][M]
     say("workload4 wgrad")
-    dw = mxq.gemm(dyt, dyts, xt, xts, d["M"], "e5m2", "e4m3", out_dtype=torch.float32)
-    sampled_check(dyt, dyts, "e5m2", xt, xts, "e4m3", d["M"], dw, torch.float32, what="wgrad")
+    dw = mxq.gemm(dyt, dyts, xt, xts, d["M"], "e5m2", "e4m3", out_dtype=torch.float32, accum=accum)
+    sampled_check(dyt, dyts, "e5m2", xt, xts, "e4m3", d["M"], dw, torch.float32, what="wgrad " + accum,
+                  strict=accum == "fp32")
 
 
+@pytest.mark.parametrize("accum", ACCS)
 @pytest.mark.parametrize("K", [4000, 4001, 4031])
-def test_workload5_ragged(K):
+def test_workload5_ragged(K, accum):
     d = wl.workload5(K=K)
     xc, xs = mxq.quantize(d["x"].to(DEV), "e4m3", "row")
     wc, ws = mxq.quantize(d["w"].to(DEV), "e4m3", "row")
     say("workload5 gemm K=%d" % K)
-    y = mxq.gemm(xc, xs, wc, ws, K, out_dtype=torch.float32)
-    sampled_check(xc, xs, "e4m3", wc, ws, "e4m3", K, y, torch.float32, what="workload5 K=%d" % K)
+    y = mxq.gemm(xc, xs, wc, ws, K, out_dtype=torch.float32, accum=accum)
+    sampled_check(xc, xs, "e4m3", wc, ws, "e4m3", K, y, torch.float32, what="workload5 K=%d %s" % (K, accum),
+                  strict=accum == "fp32")
 
 
-def test_workload1_full():
+@pytest.mark.parametrize("accum", ACCS)
+def test_workload1_full(accum):
     d = wl.workload1()
     xc, xs = mxq.quantize(d["x"].to(DEV), "e4m3", "row")
     wc, ws = mxq.quantize(d["w_kn"].to(DEV), "e4m3", "col")
-    y = mxq.gemm(xc, xs, wc, ws, d["K"], out_dtype=torch.float32)
-    full_check(xc, xs, "e4m3", wc, ws, "e4m3", d["K"], y, torch.float32, what="workload1")
+    y = mxq.gemm(xc, xs, wc, ws, d["K"], out_dtype=torch.float32, accum=accum)
+    full_check(xc, xs, "e4m3", wc, ws, "e4m3", d["K"], y, torch.float32, what="workload1 " + accum,
+               strict=accum == "fp32")
