@@ -140,7 +140,10 @@ int mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales
  *          an [N][K] weight with MXQ_ROWWISE, or a [K][N] weight with MXQ_COLWISE);
  *          w_scales [N][ld_ws], w_elem MXQ_E4M3 or MXQ_E5M2 (mixed formats allowed).
  *          ld_x, ld_w >= Kp and multiples of 16; code pointers 16-byte aligned;
- *          ld_xs, ld_ws >= nb.
+ *          ld_xs, ld_ws >= nb.  Performance: with MXQ_ACC_FP8_MFMA, scale arrays whose base
+ *          and leading dimension are multiples of 16 bytes take the fastest kernel (the
+ *          other layouts are handled by a slower one); a 16-byte aligned y with a 16-byte
+ *          multiple row pitch gets full-row stores.
  * Result   acc[i][j] = sum_b 2^(sx[i][b] + sw[j][b] - 254) * sum_{k in b, k < K}
  *                        dec(x[i][k]) * dec(w[j][k])
  *          accumulated as `accum` states (see mxq_accum; summation order is

@@ -119,6 +119,8 @@ def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None):
                 scales [cols][Kp/32] (K = rows).
     Codes are uint8 OCP bytes; scales are uint8 E8M0 bytes.  Optional preallocated
     outputs may be wider than Kp (their row stride is passed as the leading dimension).
+    Scales allocated here are a [L][Kp/32] view of rows padded to a multiple of 16 bytes,
+    the layout the fastest GEMM kernel reads.
     """
     torch = _torch()
     if x.dim() != 2:
@@ -132,7 +134,8 @@ def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None):
     if codes is None:
         codes = torch.empty((L, Kp), dtype=torch.uint8, device=x.device)
     if scales is None:
-        scales = torch.empty((L, Kp // 32), dtype=torch.uint8, device=x.device)
+        nb = Kp // 32
+        scales = torch.empty((L, _round_up(nb, 16)), dtype=torch.uint8, device=x.device)[:, :nb]
     st = mxq_quantize(x.data_ptr(), _wide_type(x), rows, cols, x.stride(0) if rows > 0 else cols, ax,
                       _ELEM[elem], codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0),
                       _stream_handle())

@@ -15,7 +15,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # no packed-fp32 VALU ops (v_pk_{add,mul,fma}_f32) anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function",
+    "-Wall", "-Wno-inline-asm", "-Wno-unused-function",
 ]
 
 

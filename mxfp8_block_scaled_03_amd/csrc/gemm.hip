@@ -372,6 +372,456 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(int M, int N, int K, int t
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Ping-pong kernel for the matrix-core accumulation mode.
+//
+// 8 waves, 256x256 output tile, 64-byte K steps, 4 LDS code stages.  Waves w and w+4
+// share a SIMD; waves 0-3 (group 0) own output rows 0-127 of the tile and waves 4-7
+// (group 1) rows 128-255, each wave a 128x64 block (4x2 MFMA tiles, 128 accumulator
+// registers).  The two groups alternate between a memory phase (issue the DMA of step
+// t+3, read step t's fragments and scales from LDS) and a compute phase (8 scaled MFMAs),
+// with one workgroup barrier between phases and group 1 shifted by one phase, so on every
+// SIMD one wave feeds the matrix core while the other waits on LDS.
+//
+// A code stage holds both tiles of one step, 256 rows x 64 bytes each, 16-byte chunk c
+// of row r stored at chunk c ^ ((r >> 2) & 3), which makes the ds_read_b128 fragment
+// reads conflict free.  Scales travel separately, 16 bytes (8 steps) per row at a time,
+// into a two-slot ring.  Tiles and scales move global -> LDS by buffer_load ... lds
+// issued from inline assembly, their completion tracked by explicit vmcnt waits (the
+// compiler would otherwise wait for every LDS DMA before each LDS read).  Bytes past a
+// row's codes and rows past the edge read as zero through the buffer bound; in the last,
+// partial step the code bytes at k >= K are zeroed in registers and the scale of a block
+// >= nb is replaced by 127.  The MFMA takes W as its A operand and X as its B operand, so
+// a lane ends up holding four consecutive output columns of one row; interior tiles are
+// written through LDS as 16-byte row segments.  Requires 16-byte aligned scale rows
+// (scale base and leading dimension).
+namespace pp {
+
+constexpr int kThreads = 512;
+constexpr int kStages = 4;
+constexpr int kCodeBytes = 256 * 64;            // one operand's codes in one stage
+constexpr int kOffB = kCodeBytes;
+constexpr int kStageBytes = 2 * kCodeBytes;     // 32 KiB
+constexpr int kOffScale = kStages * kStageBytes;
+constexpr int kScaleSlot = 2 * 256 * 16;        // A then B: 256 rows x 16 bytes each
+constexpr int kLdsBytes = kOffScale + 2 * kScaleSlot;   // 144 KiB
+constexpr int kEpiWaveBytes = 16384;            // per-wave epilogue staging (in the code stages)
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, v4i rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Raw buffer descriptor (stride 0) over [base, base + bytes), all fields wave-uniform.
+__device__ __forceinline__ v4i rsrc_of(uint64_t base, uint32_t bytes) {
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// s_waitcnt with vmcnt(n) and expcnt / lgkmcnt left at their maxima (n < 64).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// vmcnt(n) for the counts a step's DMA can leave outstanding (n <= 9).
+__device__ __forceinline__ void wait_vm_le(int n) {
+  if (n >= 9) wait_vm<9>();
+  else if (n == 8) wait_vm<8>();
+  else if (n >= 5) wait_vm<5>();
+  else if (n >= 4) wait_vm<4>();
+  else wait_vm<0>();
+}
+
+// Workgroup barrier ordering LDS accesses only (global DMA completion is handled by the
+// explicit vmcnt waits before it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+struct Dma {
+  uint64_t a_base, b_base, s_base;   // tile row 0 of X codes, W codes, this wave's scales
+  uint32_t a_bytes, b_bytes, s_bytes;
+  uint32_t voff_a0, voff_a1, voff_b0, voff_b1, voff_s;
+  uint32_t lds_a, lds_b, lds_s;      // LDS destinations (code stage 0, scale slot 0)
+  int T;
+};
+
+// VMEM instructions issue_step(s) issues per wave.
+__device__ __forceinline__ int loads_of(int s, int T) { return s < T ? 4 + ((s & 7) == 0) : 0; }
+
+// Issue step s (K bytes 64s..64s+63) into code stage s % 4: this wave's 32 rows of each
+// code tile (two 16-row loads per operand); every 8th step also this wave's 64 scale rows
+// of the next 8 steps (16 bytes per row) into scale slot (s / 8) % 2.
+__device__ __forceinline__ void issue_step(const Dma& d, int s) {
+  const uint32_t so = (uint32_t)(s & 3) * kStageBytes;
+  const uint32_t kb = 64u * (uint32_t)s;
+  const v4i ra = rsrc_of(d.a_base + kb, d.a_bytes - kb);
+  const v4i rb = rsrc_of(d.b_base + kb, d.b_bytes - kb);
+  dma16(d.lds_a + so, d.voff_a0, ra);
+  dma16(d.lds_a + so + 1024, d.voff_a1, ra);
+  dma16(d.lds_b + so, d.voff_b0, rb);
+  dma16(d.lds_b + so + 1024, d.voff_b1, rb);
+  if ((s & 7) == 0) {
+    const uint32_t ub = 2u * (uint32_t)s;          // 16 bytes per 8 steps
+    const v4i rs = rsrc_of(d.s_base + ub, d.s_bytes - ub);
+    dma16(d.lds_s + (uint32_t)((s >> 3) & 1) * kScaleSlot, d.voff_s, rs);
+  }
+}
+
+// Round-to-nearest-even float -> bf16 bits of two values, packed (lo = a).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+}
+
+template <int FA, int FB, int Y_BF16, bool BIAS>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, int tiles_m, int tiles_n,
+                                                        const uint8_t* __restrict__ xc, int64_t ld_x,
+                                                        const uint8_t* __restrict__ xs, int64_t ld_xs,
+                                                        const uint8_t* __restrict__ wc, int64_t ld_w,
+                                                        const uint8_t* __restrict__ ws, int64_t ld_ws, float alpha,
+                                                        const float* __restrict__ bias, void* __restrict__ y,
+                                                        int64_t ld_y, int y_vec16) {
+  // ---- tile selection: XCD-first, then grouped rows
+  const int ntiles = tiles_m * tiles_n;
+  const int wg = blockIdx.x;
+  int t;
+  {
+    const int xcd = wg % kXcds, local = wg / kXcds;
+    const int q = ntiles / kXcds, r = ntiles % kXcds;
+    t = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  }
+  const int per_group = kGroupM * tiles_n;
+  const int group = t / per_group;
+  const int first_m = group * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int tm = first_m + (t % per_group) % gsize;
+  const int tn = (t % per_group) / gsize;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gp = wid >> 2, wq = wid & 3;
+  const int li = lane & 31, lg = lane >> 5;
+  const int Kp = 32 * ((K + 31) / 32);
+  const int nb = Kp / 32;
+  const int T = (K + 63) / 64;
+  const int rows_a = min(BM, M - m0), rows_b = min(BN, N - n0);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
+
+  // ---- DMA set-up: wave w loads rows 32w..32w+31 of both code tiles; load n covers rows
+  //      32w + 16n + lane/4, physical chunk lane & 3 holding logical chunk
+  //      (lane & 3) ^ ((row >> 2) & 3).  Scales: waves 0-3 rows 64w + lane of X, waves 4-7
+  //      rows 64(w-4) + lane of W.
+  Dma d;
+  {
+    d.T = T;
+    d.a_base = (uint64_t)(uintptr_t)(xc + (int64_t)m0 * ld_x);
+    d.b_base = (uint64_t)(uintptr_t)(wc + (int64_t)n0 * ld_w);
+    d.a_bytes = (uint32_t)((int64_t)(rows_a - 1) * ld_x + Kp);
+    d.b_bytes = (uint32_t)((int64_t)(rows_b - 1) * ld_w + Kp);
+    const int drow = 32 * wid + (lane >> 2);
+    const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+    d.voff_a0 = (uint32_t)(drow * ld_x + 16 * dchunk);
+    d.voff_a1 = d.voff_a0 + (uint32_t)(16 * ld_x);
+    d.voff_b0 = (uint32_t)(drow * ld_w + 16 * dchunk);
+    d.voff_b1 = d.voff_b0 + (uint32_t)(16 * ld_w);
+    d.lds_a = lds0 + (uint32_t)(32 * wid) * 64;
+    d.lds_b = lds0 + kOffB + (uint32_t)(32 * wid) * 64;
+    const int nb16 = (nb + 15) & ~15;
+    const int srow = 64 * (wid & 3) + lane;
+    if (wid < 4) {
+      d.s_base = (uint64_t)(uintptr_t)(xs + (int64_t)m0 * ld_xs);
+      d.s_bytes = (uint32_t)((int64_t)(rows_a - 1) * ld_xs + nb16);
+      d.voff_s = (uint32_t)(srow * ld_xs);
+      d.lds_s = lds0 + kOffScale + (uint32_t)(64 * wid) * 16;
+    } else {
+      d.s_base = (uint64_t)(uintptr_t)(ws + (int64_t)n0 * ld_ws);
+      d.s_bytes = (uint32_t)((int64_t)(rows_b - 1) * ld_ws + nb16);
+      d.voff_s = (uint32_t)(srow * ld_ws);
+      d.lds_s = lds0 + kOffScale + 4096 + (uint32_t)(64 * (wid - 4)) * 16;
+    }
+  }
+
+  // ---- fragment read addresses (stage 0); tile f / fj adds 2048 bytes.  Scale read
+  //      addresses (slot 0): row * 16, tile f / fj adds 512 bytes.
+  const uint32_t xsw = (uint32_t)((li >> 2) & 3);
+  uint32_t ra[2], rb[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t c = (uint32_t)(2 * h + lg);
+    ra[h] = (uint32_t)(gp * 128 + li) * 64 + ((c ^ xsw) << 4);
+    rb[h] = kOffB + (uint32_t)(wq * 64 + li) * 64 + ((c ^ xsw) << 4);
+  }
+  const uint32_t rsa = kOffScale + (uint32_t)(gp * 128 + li) * 16;
+  const uint32_t rsb = kOffScale + 4096 + (uint32_t)(wq * 64 + li) * 16;
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  v8i fa[4], fb[2];
+  uint32_t sa[4], sb[2];
+
+  // memory phase of step s: DMA of step s+3, fragments and scales of step s, then wait for
+  // this wave's DMA of step s+1 (its LDS reads complete at the barrier that follows)
+  auto memory_phase = [&](int s, auto last) {
+    if (s + 3 < T) issue_step(d, s + 3);
+    const uint32_t so = (uint32_t)(s & 3) * kStageBytes;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const v4i lo = lds16(ra[0] + so, 2048 * f), hi = lds16(ra[1] + so, 2048 * f);
+      fa[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const v4i lo = lds16(rb[0] + so, 2048 * f), hi = lds16(rb[1] + so, 2048 * f);
+      fb[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    // scale dword of blocks 4u..4u+3 (u = s/2) of each fragment row; lane g uses block
+    // 2s+g, byte 2(s&1) after the shift
+    const uint32_t ss = (uint32_t)((s >> 3) & 1) * kScaleSlot + 4u * (uint32_t)((s & 7) >> 1);
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      sa[f] = *reinterpret_cast<const uint32_t*>(smem + rsa + ss + 512 * f) >> (8 * lg);
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      sb[f] = *reinterpret_cast<const uint32_t*>(smem + rsb + ss + 512 * f) >> (8 * lg);
+    if (decltype(last)::value) {
+      if ((K & 63) != 0) {
+        // dword e of a fragment holds k = 64s + 32(e/4) + 16g + 4(e%4) .. +3
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int keep = K - (64 * s + 32 * (e >> 2) + 16 * lg + 4 * (e & 3));
+          const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
+#pragma unroll
+          for (int f = 0; f < 4; ++f) fa[f][e] = (int)((uint32_t)fa[f][e] & m);
+#pragma unroll
+          for (int f = 0; f < 2; ++f) fb[f][e] = (int)((uint32_t)fb[f][e] & m);
+        }
+      }
+      if (2 * s + lg >= nb) {
+        const uint32_t sh = 16u * (uint32_t)(s & 1);
+        const uint32_t keep = ~(0xFFu << sh), one = 127u << sh;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) sa[f] = (sa[f] & keep) | one;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) sb[f] = (sb[f] & keep) | one;
+      }
+    }
+    wait_vm_le(loads_of(s + 2, T) + loads_of(s + 3, T));
+  };
+
+  // The empty volatile asm statements pin the phase in place: the MFMAs take their
+  // operands only after the barrier that opens the phase and finish issuing before the
+  // barrier that closes it (the compiler would otherwise sink them into the next memory
+  // phase, which defeats the alternation).
+  auto compute_phase = [&](auto par) {
+    constexpr int OPS = 2 * decltype(par)::value;
+    asm volatile("" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]));
+    asm volatile("" : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sb[0]), "+v"(sb[1]));
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < 2; ++fj)
+        acc[fi][fj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[fj], fa[fi], acc[fi][fj], FB, FA, OPS,
+                                                                      (int)sb[fj], OPS, (int)sa[fi]);
+    asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+    asm volatile("" : "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1]));
+  };
+
+  // ---- prologue: steps 0..2 in flight, step 0 landed everywhere
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+    if (s < T) issue_step(d, s);
+  wait_vm_le(loads_of(1, T) + loads_of(2, T));
+  lds_barrier();
+  if (gp == 1) lds_barrier();   // group 1 runs one phase behind group 0
+
+  // one K step: memory phase, barrier, compute phase, barrier
+  auto step = [&](int s, auto par, auto last) {
+    __builtin_amdgcn_sched_barrier(0);
+    memory_phase(s, last);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    compute_phase(par);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using No = std::false_type;
+  using Yes = std::true_type;
+  // steps 0..T-2 in pairs (even step: opsel byte 0, odd: byte 2); the last step, which
+  // may be partial, on its own
+  int s = 0;
+  for (; s + 2 <= T - 1; s += 2) {
+    step(s, C0(), No());
+    step(s + 1, C1(), No());
+  }
+  if (s < T - 1) {
+    step(s, C0(), No());
+    ++s;
+  }
+  if (T > 0) {
+    if (s & 1)
+      step(s, C1(), Yes());
+    else
+      step(s, C0(), Yes());
+  }
+  if (gp == 0) lds_barrier();   // matches group 1's extra barrier: all LDS reads are done
+
+  // ---- epilogue: y = alpha * acc + bias[col], rounded once to the output type.  Lane
+  //      (g, i) holds Y[row 32 fi + i][col 32 fj + 8 q + 4 g + e] in acc[fi][fj][4 q + e]
+  //      (rows and columns relative to the wave's 128x64 block).
+  const int wrow0 = m0 + gp * 128, wcol0 = n0 + wq * 64;
+  auto value = [&](int fi, int fj, int r, float bv) {
+    return BIAS ? __builtin_fmaf(alpha, acc[fi][fj][r], bv) : alpha * acc[fi][fj][r];
+  };
+  if (y_vec16 && m0 + BM <= M && n0 + BN <= N) {
+    // stage the block in this wave's LDS region as row-major rows of 64 values with the
+    // 16-byte chunk index XOR (row & 7), then store whole 16-byte row pieces
+    constexpr int E = Y_BF16 ? 2 : 4;                // bytes per value
+    constexpr int RB = 64 * E;                       // bytes per staged row
+    constexpr int CPR = RB / 16;                     // 16-byte chunks per row
+    constexpr int RP = kEpiWaveBytes / RB;           // rows per pass: 128 (bf16) or 64 (fp32)
+    constexpr int FPP = RP / 32;                     // fragment rows per pass
+    const uint32_t wbase = (uint32_t)wid * kEpiWaveBytes;
+#pragma unroll
+    for (int pass = 0; pass < 128 / RP; ++pass) {
+#pragma unroll
+      for (int fj = 0; fj < 2; ++fj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c0 = 32 * fj + 8 * q + 4 * lg;   // first of this lane's 4 columns
+          float bv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (BIAS) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bv[e] = bias[wcol0 + c0 + e];
+          }
+#pragma unroll
+          for (int fl = 0; fl < FPP; ++fl) {
+            const int fi = pass * FPP + fl;
+            const int row = 32 * fl + li;
+            const uint32_t byte = (uint32_t)(c0 * E);
+            const uint32_t chunk = (byte >> 4) ^ (uint32_t)(row & (CPR - 1) & 7);
+            const uint32_t addr = wbase + (uint32_t)row * RB + (chunk << 4) + (byte & 15);
+            if (Y_BF16) {
+              typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+              v2u p;
+              p[0] = pack_bf16(value(fi, fj, 4 * q + 0, bv[0]), value(fi, fj, 4 * q + 1, bv[1]));
+              p[1] = pack_bf16(value(fi, fj, 4 * q + 2, bv[2]), value(fi, fj, 4 * q + 3, bv[3]));
+              *reinterpret_cast<v2u*>(smem + addr) = p;
+            } else {
+              typedef float v4f __attribute__((ext_vector_type(4)));
+              v4f p;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) p[e] = value(fi, fj, 4 * q + e, bv[e]);
+              *reinterpret_cast<v4f*>(smem + addr) = p;
+            }
+          }
+        }
+      // read back 16 bytes per lane: 64 lanes cover 1024 bytes = 1024 / RB rows
+      constexpr int RPI = 1024 / RB;
+#pragma unroll
+      for (int it = 0; it < RP / RPI; ++it) {
+        const int row = it * RPI + lane / CPR;
+        const int c = lane % CPR;
+        const uint32_t addr = wbase + (uint32_t)row * RB + (uint32_t)((c ^ (row & (CPR - 1) & 7)) << 4);
+        const v4i v = *reinterpret_cast<const v4i*>(smem + addr);
+        uint8_t* dst = reinterpret_cast<uint8_t*>(y) +
+                       ((int64_t)(wrow0 + pass * RP + row) * ld_y + wcol0) * E + 16 * c;
+        *reinterpret_cast<v4i*>(dst) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int fj = 0; fj < 2; ++fj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = wcol0 + 32 * fj + 8 * q + 4 * lg + e;
+          const float bv = (BIAS && col < N) ? bias[col] : 0.0f;
+#pragma unroll
+          for (int fi = 0; fi < 4; ++fi) {
+            const int row = wrow0 + 32 * fi + li;
+            if (row < M && col < N) {
+              const float v = value(fi, fj, 4 * q + e, bv);
+              if (Y_BF16)
+                reinterpret_cast<uint16_t*>(y)[(int64_t)row * ld_y + col] = (uint16_t)f32_to_bf16_rne(v);
+              else
+                reinterpret_cast<float*>(y)[(int64_t)row * ld_y + col] = v;
+            }
+          }
+        }
+  }
+}
+
+template <int FA, int FB, int Y_BF16, bool BIAS>
+hipError_t launch_t(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
+                    int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, float alpha,
+                    const float* bias, void* y, int64_t ld_y, hipStream_t stream) {
+  static bool attr_set[64] = {false};
+  auto kern = k_gemm_pp<FA, FB, Y_BF16, BIAS>;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!attr_set[dev]) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set[dev] = true;
+  }
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  const int E = Y_BF16 ? 2 : 4;
+  const int y_vec16 = ((uintptr_t)y % 16 == 0) && ((ld_y * E) % 16 == 0);
+  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreads), kLdsBytes, stream, (int)M, (int)N, (int)K, tiles_m,
+                     tiles_n, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, y_vec16);
+  return hipGetLastError();
+}
+
+template <int FA, int FB>
+hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
+                    int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, float alpha,
+                    const float* bias, void* y, int y_bf16, int64_t ld_y, hipStream_t stream) {
+  if (y_bf16) {
+    if (bias) return launch_t<FA, FB, 1, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
+    return launch_t<FA, FB, 1, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
+  }
+  if (bias) return launch_t<FA, FB, 0, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
+  return launch_t<FA, FB, 0, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
+}
+
+hipError_t launch(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
+                  int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, int w_fmt, float alpha,
+                  const float* bias, void* y, int y_bf16, int64_t ld_y, hipStream_t stream) {
+  if (x_fmt == kE4M3 && w_fmt == kE4M3)
+    return launch_f<0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
+  if (x_fmt == kE4M3)
+    return launch_f<0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
+  if (w_fmt == kE4M3)
+    return launch_f<1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
+  return launch_f<1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
+}
+
+}  // namespace pp
+
 template <int MODE, int FA, int FB, int Y_BF16, bool BIAS>
 hipError_t gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
                   const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, float alpha, const float* bias,
@@ -423,6 +873,10 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64
                        int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
                        int w_fmt, float alpha, const float* bias, void* y, int y_bf16, int64_t ld_y, int exact,
                        hipStream_t stream) {
+  const bool scales16 = ((uintptr_t)xs % 16 == 0) && ((uintptr_t)ws % 16 == 0) && ld_xs % 16 == 0 && ld_ws % 16 == 0;
+  if (!exact && scales16)
+    return pp::launch(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, alpha, bias, y, y_bf16, ld_y,
+                      stream);
   if (exact)
     return gemm_m<1>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, alpha, bias, y, y_bf16, ld_y, stream);
   return gemm_m<0>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, alpha, bias, y, y_bf16, ld_y, stream);

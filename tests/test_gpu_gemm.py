@@ -96,6 +96,37 @@ def test_gemm_ignores_bytes_past_k(accum):
     assert torch.equal(y0, y1)
 
 
+def strided_scales(s, ld, offset=0):
+    """Copy of a [rows][nb] scale array stored with leading dimension ld, starting `offset`
+    bytes into its buffer (offset 1 makes every row start unaligned)."""
+    rows, nb = s.shape
+    buf = torch.full((rows * ld + offset + 8,), 255, dtype=torch.uint8, device=DEV)
+    view = buf[offset:offset + rows * ld].view(rows, ld)[:, :nb]
+    view.copy_(s)
+    return view
+
+
+@pytest.mark.parametrize("layout", ["ld%16", "ld%4", "ld odd", "unaligned"])
+@pytest.mark.parametrize("M,N,K", [(300, 260, 4000), (257, 300, 96), (130, 70, 33), (64, 520, 4001)])
+def test_gemm_scale_layouts(M, N, K, layout):
+    """Scale rows with a 16-byte aligned base and leading dimension take the ping-pong
+    kernel, the others the 4-wave one; both must meet the contract bound."""
+    say("gemm scale layout %s %dx%dx%d" % (layout, M, N, K))
+    rng = np.random.default_rng(11)
+    xc, xs = quantized(rng, M, K, 1.0, "e4m3")
+    wc, ws = quantized(rng, N, K, 0.02, "e4m3")
+    nb = xs.shape[1]
+    ld = {"ld%16": (nb + 15) // 16 * 16 + 16, "ld%4": (nb + 3) // 4 * 4 + 4 + 8 * ((nb + 3) // 4 % 2 == 0),
+          "ld odd": nb + 1 + (nb % 2), "unaligned": nb + 4}[layout]
+    off = 1 if layout == "unaligned" else 0
+    xs2, ws2 = strided_scales(xs, ld, off), strided_scales(ws, ld, off)
+    y = mxq.gemm(xc, xs2, wc, ws2, K, out_dtype=torch.float32)
+    y0 = mxq.gemm(xc, xs, wc, ws, K, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    full_check(xc, xs, "e4m3", wc, ws, "e4m3", K, y, torch.float32, what="layout " + layout)
+    full_check(xc, xs, "e4m3", wc, ws, "e4m3", K, y0, torch.float32, what="padded scales")
+
+
 @pytest.mark.parametrize("accum", ACCS)
 def test_gemm_two_row_fixture(accum):
     from conftest import load_golden
