@@ -404,7 +404,8 @@ constexpr int kOffB = kCodeBytes;
 constexpr int kStageBytes = 2 * kCodeBytes;     // 32 KiB
 constexpr int kOffScale = kStages * kStageBytes;
 constexpr int kScaleSlot = 2 * 256 * 16;        // A then B: 256 rows x 16 bytes each
-constexpr int kLdsBytes = kOffScale + 2 * kScaleSlot;   // 144 KiB
+constexpr int kOffJunk = kOffScale + 2 * kScaleSlot;    // target of the idle scale loads
+constexpr int kLdsBytes = kOffJunk + 1024;               // 145 KiB
 constexpr int kEpiWaveBytes = 16384;            // per-wave epilogue staging (in the code stages)
 
 #pragma clang diagnostic push
@@ -434,15 +435,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// vmcnt(n) for the counts a step's DMA can leave outstanding (n <= 9).
-__device__ __forceinline__ void wait_vm_le(int n) {
-  if (n >= 9) wait_vm<9>();
-  else if (n == 8) wait_vm<8>();
-  else if (n >= 5) wait_vm<5>();
-  else if (n >= 4) wait_vm<4>();
-  else wait_vm<0>();
-}
-
 // Workgroup barrier ordering LDS accesses only (global DMA completion is handled by the
 // explicit vmcnt waits before it).
 __device__ __forceinline__ void lds_barrier() {
@@ -456,29 +448,74 @@ struct Dma {
   uint32_t a_bytes, b_bytes, s_bytes;
   uint32_t voff_a0, voff_a1, voff_b0, voff_b1, voff_s;
   uint32_t lds_a, lds_b, lds_s;      // LDS destinations (code stage 0, scale slot 0)
+  uint32_t lds_junk;
   int T;
 };
 
-// VMEM instructions issue_step(s) issues per wave.
-__device__ __forceinline__ int loads_of(int s, int T) { return s < T ? 4 + ((s & 7) == 0) : 0; }
+// Every step's DMA is 5 loads per wave, so the waits below are constants: kLoadsPerStep.
+// Step s (K bytes 64s..64s+63) goes into code stage s % 4: this wave's 32 rows of each
+// code tile (two 16-row loads per operand); every 8th step the fifth load brings this
+// wave's 64 scale rows of the next 8 steps (16 bytes per row) into scale slot (s / 8) % 2,
+// the other steps it is an empty load into a junk area.  Steps s >= T get an empty buffer
+// range: they only write zeros into a stage (or scale slot) that is never read again.
+// Keeping every step's issue pattern identical and branch free also keeps each phase in
+// one basic block, where the scheduling barriers hold the MFMAs in place.
+constexpr int kLoadsPerStep = 5;
+struct StepDma {
+  v4i ra, rb;
+  uint32_t so;
+};
 
-// Issue step s (K bytes 64s..64s+63) into code stage s % 4: this wave's 32 rows of each
-// code tile (two 16-row loads per operand); every 8th step also this wave's 64 scale rows
-// of the next 8 steps (16 bytes per row) into scale slot (s / 8) % 2.
+__device__ __forceinline__ StepDma step_dma(const Dma& d, int s) {
+  const bool live = s < d.T;
+  const uint32_t kb = live ? 64u * (uint32_t)s : 0u;
+  return StepDma{rsrc_of(d.a_base + kb, live ? d.a_bytes - kb : 0u), rsrc_of(d.b_base + kb, live ? d.b_bytes - kb : 0u),
+                 (uint32_t)(s & 3) * kStageBytes};
+}
+
+__device__ __forceinline__ void issue_code(const Dma& d, const StepDma& sd, int n) {
+  if (n == 0) dma16(d.lds_a + sd.so, d.voff_a0, sd.ra);
+  if (n == 1) dma16(d.lds_a + sd.so + 1024, d.voff_a1, sd.ra);
+  if (n == 2) dma16(d.lds_b + sd.so, d.voff_b0, sd.rb);
+  if (n == 3) dma16(d.lds_b + sd.so + 1024, d.voff_b1, sd.rb);
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// dma16 placed between two MFMAs: it names `after` (an operand of the MFMAs before it)
+// and `before` (an operand of the MFMAs after it) as read-write operands it never touches,
+// which orders it after the last reader of `after` and before the first reader of
+// `before` without any hardware dependency.  (Only operands are named: naming an MFMA
+// result would make the compiler copy it while the MFMA is still writing it.)
+__device__ __forceinline__ void dma16_between(uint32_t lds, uint32_t voff, v4i rsrc, v8i& after, v8i& before) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %3, %4, 0 offen lds"
+               : "+v"(after), "+v"(before)
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// The same after the last MFMA that reads `after`.
+__device__ __forceinline__ void dma16_after(uint32_t lds, uint32_t voff, v4i rsrc, v8i& after) {
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
+               : "+v"(after)
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void issue_scales(const Dma& d, int s) {
+  const bool real = (s & 7) == 0;
+  const bool live = real && s < d.T;
+  const uint32_t ub = live ? 2u * (uint32_t)s : 0u;    // 16 bytes per 8 steps
+  const v4i rs = rsrc_of(d.s_base + ub, live ? d.s_bytes - ub : 0u);
+  dma16(real ? d.lds_s + (uint32_t)((s >> 3) & 1) * kScaleSlot : d.lds_junk, d.voff_s, rs);
+}
+
 __device__ __forceinline__ void issue_step(const Dma& d, int s) {
-  const uint32_t so = (uint32_t)(s & 3) * kStageBytes;
-  const uint32_t kb = 64u * (uint32_t)s;
-  const v4i ra = rsrc_of(d.a_base + kb, d.a_bytes - kb);
-  const v4i rb = rsrc_of(d.b_base + kb, d.b_bytes - kb);
-  dma16(d.lds_a + so, d.voff_a0, ra);
-  dma16(d.lds_a + so + 1024, d.voff_a1, ra);
-  dma16(d.lds_b + so, d.voff_b0, rb);
-  dma16(d.lds_b + so + 1024, d.voff_b1, rb);
-  if ((s & 7) == 0) {
-    const uint32_t ub = 2u * (uint32_t)s;          // 16 bytes per 8 steps
-    const v4i rs = rsrc_of(d.s_base + ub, d.s_bytes - ub);
-    dma16(d.lds_s + (uint32_t)((s >> 3) & 1) * kScaleSlot, d.voff_s, rs);
-  }
+  const StepDma sd = step_dma(d, s);
+#pragma unroll
+  for (int n = 0; n < 4; ++n) issue_code(d, sd, n);
+  issue_scales(d, s);
 }
 
 // Round-to-nearest-even float -> bf16 bits of two values, packed (lo = a).
@@ -540,6 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
     d.voff_b1 = d.voff_b0 + (uint32_t)(16 * ld_w);
     d.lds_a = lds0 + (uint32_t)(32 * wid) * 64;
     d.lds_b = lds0 + kOffB + (uint32_t)(32 * wid) * 64;
+    d.lds_junk = lds0 + kOffJunk;
     const int nb16 = (nb + 15) & ~15;
     const int srow = 64 * (wid & 3) + lane;
     if (wid < 4) {
@@ -579,10 +617,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
   v8i fa[4], fb[2];
   uint32_t sa[4], sb[2];
 
-  // memory phase of step s: DMA of step s+3, fragments and scales of step s, then wait for
-  // this wave's DMA of step s+1 (its LDS reads complete at the barrier that follows)
-  auto memory_phase = [&](int s, auto last) {
-    if (s + 3 < T) issue_step(d, s + 3);
+  // memory phase of step s: fragments and scales of step s, then wait for this wave's DMA
+  // of step s+1 (its LDS reads complete at the barrier that follows); only the DMA of step
+  // s+2 stays in flight (issued in the previous compute phase, or by the prologue)
+  auto memory_phase = [&](int s, auto par, auto last) {
     const uint32_t so = (uint32_t)(s & 3) * kStageBytes;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
@@ -594,15 +632,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
       const v4i lo = lds16(rb[0] + so, 2048 * f), hi = lds16(rb[1] + so, 2048 * f);
       fb[f] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    // scale dword of blocks 4u..4u+3 (u = s/2) of each fragment row; lane g uses block
-    // 2s+g, byte 2(s&1) after the shift
-    const uint32_t ss = (uint32_t)((s >> 3) & 1) * kScaleSlot + 4u * (uint32_t)((s & 7) >> 1);
+    // scale dword of blocks 4u..4u+3 (u = s/2) of each fragment row, read at even steps
+    // and kept for the odd one; lane g uses block 2s+g, byte 2(s&1) after the shift
+    if (decltype(par)::value == 0) {
+      const uint32_t ss = (uint32_t)((s >> 3) & 1) * kScaleSlot + 4u * (uint32_t)((s & 7) >> 1);
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      sa[f] = *reinterpret_cast<const uint32_t*>(smem + rsa + ss + 512 * f) >> (8 * lg);
+      for (int f = 0; f < 4; ++f)
+        sa[f] = *reinterpret_cast<const uint32_t*>(smem + rsa + ss + 512 * f) >> (8 * lg);
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
-      sb[f] = *reinterpret_cast<const uint32_t*>(smem + rsb + ss + 512 * f) >> (8 * lg);
+      for (int f = 0; f < 2; ++f)
+        sb[f] = *reinterpret_cast<const uint32_t*>(smem + rsb + ss + 512 * f) >> (8 * lg);
+    }
     if (decltype(last)::value) {
       if ((K & 63) != 0) {
         // dword e of a fragment holds k = 64s + 32(e/4) + 16g + 4(e%4) .. +3
@@ -625,43 +665,63 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
         for (int f = 0; f < 2; ++f) sb[f] = (sb[f] & keep) | one;
       }
     }
-    wait_vm_le(loads_of(s + 2, T) + loads_of(s + 3, T));
+    if (decltype(last)::value)
+      wait_vm<0>();    // also the empty loads of steps T and T+1
+    else
+      wait_vm<kLoadsPerStep>();
   };
 
-  // The empty volatile asm statements pin the phase in place: the MFMAs take their
-  // operands only after the barrier that opens the phase and finish issuing before the
-  // barrier that closes it (the compiler would otherwise sink them into the next memory
-  // phase, which defeats the alternation).
-  auto compute_phase = [&](auto par) {
+  // Compute phase of step s: 8 MFMAs, with this wave's DMA of step s+3 (whose stage was
+  // last read in the phase before) issued between them, one load after every second MFMA,
+  // so the address unit sees a steady stream instead of a burst; the last step issues none.
+  // The empty volatile asm statements make the MFMAs take their operands only after the
+  // barrier that opens the phase.  (Results are never routed through such statements:
+  // the compiler would then miss the MFMA result latency when it reads them.)
+  auto compute_phase = [&](int s, auto par, auto with_dma) {
     constexpr int OPS = 2 * decltype(par)::value;
+    constexpr bool DMA = decltype(with_dma)::value;
+    StepDma sd;
+    if (DMA) {
+      sd = step_dma(d, s + 3);
+      issue_scales(d, s + 3);
+    }
     asm volatile("" : "+v"(fa[0]), "+v"(fa[1]), "+v"(fa[2]), "+v"(fa[3]), "+v"(fb[0]), "+v"(fb[1]));
     asm volatile("" : "+v"(sa[0]), "+v"(sa[1]), "+v"(sa[2]), "+v"(sa[3]), "+v"(sb[0]), "+v"(sb[1]));
 #pragma unroll
     for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
-      for (int fj = 0; fj < 2; ++fj)
+      for (int fj = 0; fj < 2; ++fj) {
         acc[fi][fj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[fj], fa[fi], acc[fi][fj], FB, FA, OPS,
                                                                       (int)sb[fj], OPS, (int)sa[fi]);
-    asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
-    asm volatile("" : "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1]));
+        if (DMA && fj == 1 && fi < 3) {
+          // load fi of the step's DMA, between MFMA (fi, 1) and MFMA (fi + 1, 0)
+          const uint32_t lds = fi == 0 ? d.lds_a + sd.so : fi == 1 ? d.lds_a + sd.so + 1024 : d.lds_b + sd.so;
+          const uint32_t voff = fi == 0 ? d.voff_a0 : fi == 1 ? d.voff_a1 : d.voff_b0;
+          dma16_between(lds, voff, fi < 2 ? sd.ra : sd.rb, fa[fi], fa[fi + 1]);
+        }
+        if (DMA && fj == 1 && fi == 3) dma16_after(d.lds_b + sd.so + 1024, d.voff_b1, sd.rb, fa[3]);
+      }
   };
 
   // ---- prologue: steps 0..2 in flight, step 0 landed everywhere
 #pragma unroll
   for (int s = 0; s < 3; ++s)
-    if (s < T) issue_step(d, s);
-  wait_vm_le(loads_of(1, T) + loads_of(2, T));
+    issue_step(d, s);
+  if (T > 0)
+    wait_vm<2 * kLoadsPerStep>();
+  else
+    wait_vm<0>();   // K = 0: no step waits for the empty loads before the epilogue uses LDS
   lds_barrier();
   if (gp == 1) lds_barrier();   // group 1 runs one phase behind group 0
 
   // one K step: memory phase, barrier, compute phase, barrier
   auto step = [&](int s, auto par, auto last) {
     __builtin_amdgcn_sched_barrier(0);
-    memory_phase(s, last);
+    memory_phase(s, par, last);
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    compute_phase(par);
+    compute_phase(s, par, std::integral_constant<bool, !decltype(last)::value>());
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
   };
