@@ -26,14 +26,6 @@ typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 
-// Max over 32-bit patterns of the four lanes of a quad (quad_perm DPP: 1,0,3,2 then 2,3,0,1).
-__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
-  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
-  v = v > o ? v : o;
-  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
-  return v > o ? v : o;
-}
-
 __device__ __forceinline__ uint32_t pk_abs_max_bf16(uint32_t acc, uint32_t w) {
   v2u16 a = __builtin_bit_cast(v2u16, acc);
   v2u16 b = __builtin_bit_cast(v2u16, w & 0x7FFF7FFFu);
@@ -169,43 +161,40 @@ __device__ __forceinline__ void load_chunk(Chunk<SRC_BF16>& c, const void* line,
   }
 }
 
-// One quad (4 lanes) per 32-element block, 8 consecutive elements per lane.  Blocks are
-// numbered g = row * nb + b; FLAT problems are one dense run so row = 0, b = g.  Each
-// thread keeps U blocks in flight (loads first, then reduce + encode + store).
+// One lane per 32-element block: the lane loads the block's 64 (bf16) or 128 (fp32) bytes
+// with 16-byte loads, reduces the amax in registers, encodes with 16 two-value
+// conversions and stores 32 code bytes with two 16-byte stores; a wave covers 64
+// consecutive blocks, so its 64 scale bytes form one contiguous run.  Blocks are
+// numbered g = row * nb + b (FLAT problems are one dense run: row 0, b = g).  One block
+// per thread and a large grid keep enough loads in flight to stream HBM.
 template <int SRC_BF16, int F, bool FLAT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(const void* __restrict__ src, int64_t ld_src, int64_t K,
                                                         int64_t nb, int64_t nblocks, uint8_t* __restrict__ codes,
                                                         int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales) {
-  constexpr int U = 4;
   constexpr int ES = SRC_BF16 ? 2 : 4;
-  const int q = threadIdx.x & 3;
-  const int64_t stride = (int64_t)gridDim.x * (kThreads / 4);
-  for (int64_t g0 = (int64_t)blockIdx.x * (kThreads / 4) + (threadIdx.x >> 2); g0 < nblocks; g0 += stride * U) {
-    Chunk<SRC_BF16> c[U];
-    int64_t row[U], b[U];
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < nblocks; g += stride) {
+    const int64_t row = FLAT ? 0 : g / nb;
+    const int64_t b = FLAT ? g : g - row * nb;
+    const char* line = reinterpret_cast<const char*>(src) + row * ld_src * ES;
+    Chunk<SRC_BF16> c[4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t g = g0 + u * stride;
-      if (FLAT) { row[u] = 0; b[u] = g; }
-      else { row[u] = g / nb; b[u] = g - row[u] * nb; }
-      if (g < nblocks) {
-        const char* line = reinterpret_cast<const char*>(src) + row[u] * ld_src * ES;
-        // a flat problem has no partial chunks: every chunk index is in range
-        load_chunk<SRC_BF16, VEC>(c[u], line, 32 * b[u] + 8 * q, FLAT ? (int64_t)INT64_MAX : K);
-      }
-    }
+    for (int q = 0; q < 4; ++q)
+      load_chunk<SRC_BF16, VEC>(c[q], line, 32 * b + 8 * q, FLAT ? (int64_t)INT64_MAX : K);
+    uint32_t amax = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t g = g0 + u * stride;
-      if (g < nblocks) {
-        uint32_t amax = quad_max(chunk_abs_max<SRC_BF16>(c[u]));
-        uint32_t sb = scale_byte_from_amax<F>(amax);
-        uint32_t d0, d1;
-        encode_chunk<SRC_BF16, F>(c[u], sb, d0, d1);
-        *reinterpret_cast<uint2*>(codes + row[u] * ld_codes + 32 * b[u] + 8 * q) = make_uint2(d0, d1);
-        if (q == 0) scales[row[u] * ld_scales + b[u]] = (uint8_t)sb;
-      }
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = chunk_abs_max<SRC_BF16>(c[q]);
+      amax = amax > a ? amax : a;
     }
+    const uint32_t sb = scale_byte_from_amax<F>(amax);
+    uint32_t d[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) encode_chunk<SRC_BF16, F>(c[q], sb, d[2 * q], d[2 * q + 1]);
+    uint4* out = reinterpret_cast<uint4*>(codes + row * ld_codes + 32 * b);
+    out[0] = make_uint4(d[0], d[1], d[2], d[3]);
+    out[1] = make_uint4(d[4], d[5], d[6], d[7]);
+    scales[row * ld_scales + b] = (uint8_t)sb;
   }
 }
 
@@ -303,8 +292,8 @@ static hipError_t quant_rows_t(const void* src, int64_t rows, int64_t K, int64_t
                                hipStream_t stream) {
   const int64_t nb = (K + 31) / 32;
   const int64_t nblocks = rows * nb;
-  const int64_t wg_needed = (nblocks + 63) / 64;
-  const int64_t cap = (int64_t)device_cu_count() * 8;
+  const int64_t wg_needed = (nblocks + kThreads - 1) / kThreads;
+  const int64_t cap = (int64_t)device_cu_count() * 256;   // beyond this, threads loop
   const int grid = (int)(wg_needed < cap ? wg_needed : cap);
   if (flat && vec)
     hipLaunchKernelGGL((k_quant_rows<SRC_BF16, F, true, true>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src, K,
