@@ -10,11 +10,16 @@ timed on its own with HIP events around each of its launches inside the timed re
 dense MXFP8 matrix-core peak; the standalone quantize of 2^28 bf16 elements is reported
 against the HBM peak.  The CPU oracle is timed on a bounded sample of the same step.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-calibration]
+
+--copy-calibration adds a plain elementwise copy of a known size (256 MiB read, 256 MiB
+written) after the measurement, so that one hardware-counter run sees both the GEMM and a
+kernel whose HBM traffic is known; the ratio calibrates FETCH_SIZE / WRITE_SIZE.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -36,16 +41,28 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
+    p.add_argument("--copy-calibration", action="store_true", help="also run a copy of known size (counter runs)")
     return p.parse_args()
 
 
+GEMM_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_03_amd", "csrc", "gemm.hip")
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
 def load_traffic(kernel: str):
-    """HBM bytes per launch measured with rocprofv3 counters (see profiles/), or None."""
+    """HBM bytes per launch of `kernel` measured with rocprofv3 counters (profiles/), or
+    None when there is no measurement or the kernel source changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        return t.get(kernel)
-    except (OSError, ValueError):
+            t = json.load(f)[kernel]
+        if t.get("source_sha256") != source_digest(GEMM_SOURCE):
+            return None
+        return int(t["bytes_per_launch"])
+    except (OSError, ValueError, KeyError, TypeError):
         return None
 
 
@@ -78,12 +95,28 @@ def main():
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
+    # The step calls the C entry points directly with arguments prepared once, so the host
+    # enqueues far faster than the GPU runs and no host gap lands between the events.
+    import ctypes
+    L = mxq.lib()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    q_x = (x.data_ptr(), mxq.MXQ_BF16, M, K, x.stride(0), mxq.MXQ_ROWWISE, mxq.MXQ_E4M3, xc.data_ptr(), xc.stride(0),
+           xs.data_ptr(), xs.stride(0), sh)
+    q_w = (w.data_ptr(), mxq.MXQ_BF16, N, K, w.stride(0), mxq.MXQ_ROWWISE, mxq.MXQ_E4M3, wc.data_ptr(), wc.stride(0),
+           ws.data_ptr(), ws.stride(0), sh)
+    g_args = (M, N, K, xc.data_ptr(), xc.stride(0), xs.data_ptr(), xs.stride(0), mxq.MXQ_E4M3, wc.data_ptr(),
+              wc.stride(0), ws.data_ptr(), ws.stride(0), mxq.MXQ_E4M3, ctypes.c_float(1.0), None, y.data_ptr(),
+              mxq.MXQ_BF16, y.stride(0), mxq.MXQ_ACC_FP8_MFMA, sh)
+    for a in (L.mxq_quantize(*q_x), L.mxq_quantize(*q_w), L.mxq_gemm(*g_args)):
+        if a != 0:
+            raise RuntimeError("mxq call failed: %s" % mxq.mxq_status_string(a))
+
     def step(ev=None):
-        mxq.quantize(x, "e4m3", "row", codes=xc, scales=xs)
-        mxq.quantize(w, "e4m3", "row", codes=wc, scales=ws)
+        L.mxq_quantize(*q_x)
+        L.mxq_quantize(*q_w)
         if ev is not None:
             ev[0].record(stream)
-        mxq.gemm(xc, xs, wc, ws, K, out=y)
+        L.mxq_gemm(*g_args)
         if ev is not None:
             ev[1].record(stream)
 
@@ -112,12 +145,15 @@ def main():
 
     # ---- the same GEMM with exact-product FP32 accumulation (meets the 1e-5*T bound)
     ye = torch.empty_like(y)
+    ge_args = list(g_args)
+    ge_args[15] = ye.data_ptr()
+    ge_args[18] = mxq.MXQ_ACC_FP32
     for _ in range(3):
-        mxq.gemm(xc, xs, wc, ws, K, out=ye, accum="fp32")
+        L.mxq_gemm(*ge_args)
     ee = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
     for a, b in ee:
         a.record(stream)
-        mxq.gemm(xc, xs, wc, ws, K, out=ye, accum="fp32")
+        L.mxq_gemm(*ge_args)
         b.record(stream)
     torch.cuda.synchronize()
     exact_ms = sum(a.elapsed_time(b) for a, b in ee) / len(ee)
@@ -130,14 +166,16 @@ def main():
     del q
     qc = torch.empty((qx.shape[0], qx.shape[1]), dtype=torch.uint8, device=dev)
     qs = torch.empty((qx.shape[0], qx.shape[1] // 32), dtype=torch.uint8, device=dev)
+    q_q = (qx.data_ptr(), mxq.MXQ_BF16, qx.shape[0], qx.shape[1], qx.stride(0), mxq.MXQ_ROWWISE, mxq.MXQ_E4M3,
+           qc.data_ptr(), qc.stride(0), qs.data_ptr(), qs.stride(0), sh)
     for _ in range(3):
-        mxq.quantize(qx, "e4m3", "row", codes=qc, scales=qs)
+        L.mxq_quantize(*q_q)
     torch.cuda.synchronize()
     nq = 20
     qe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nq)]
     for a, b in qe:
         a.record(stream)
-        mxq.quantize(qx, "e4m3", "row", codes=qc, scales=qs)
+        L.mxq_quantize(*q_q)
         b.record(stream)
     torch.cuda.synchronize()
     q_ms = sum(a.elapsed_time(b) for a, b in qe) / nq
@@ -146,13 +184,15 @@ def main():
     del qx, qc, qs
 
     # quantize of the step's X alone (8192 x 4096 bf16)
-    xq_e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
-    for a, b in xq_e:
-        a.record(stream)
-        mxq.quantize(x, "e4m3", "row", codes=xc, scales=xs)
-        b.record(stream)
+    # X alone: 20 launches between two events (a single launch is short enough that the
+    # host could fall behind the GPU)
+    xa, xb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    xa.record(stream)
+    for _ in range(20):
+        L.mxq_quantize(*q_x)
+    xb.record(stream)
     torch.cuda.synchronize()
-    xq_ms = sum(a.elapsed_time(b) for a, b in xq_e) / len(xq_e)
+    xq_ms = xa.elapsed_time(xb) / 20
     xq_gbs = M * K * (2 + 1 + 1 / 32) / (xq_ms * 1e-3) / 1e9
 
     traffic = load_traffic("gemm")
@@ -185,6 +225,14 @@ def main():
                               "bytes": int(q_bytes), "workload": "[16384][16384] bf16 Laplace(0,1) 1% x1e4, rowwise E4M3"},
         },
     }
+
+    if args.copy_calibration:
+        a = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(2):
+            torch.mul(a, 1.0, out=b)      # reads 256 MiB, writes 256 MiB
+        torch.cuda.synchronize()
+        del a, b
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(d, xc, xs, wc, ws, M, N, K, args.cpu_seconds)
