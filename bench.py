@@ -181,7 +181,32 @@ def main():
     q_ms = sum(a.elapsed_time(b) for a, b in qe) / nq
     q_bytes = qx.numel() * (2 + 1 + 1 / 32)
     q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
-    del qx, qc, qs
+
+    # secondary quantize rows on the same 2^28 input: rowwise E5M2, columnwise E4M3
+    # (codes [cols][rows]), and dequantize of the rowwise codes back to bf16
+    def time_calls(fn, n=10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    q_e5 = list(q_q)
+    q_e5[6] = mxq.MXQ_E5M2
+    e5_ms = time_calls(lambda: L.mxq_quantize(*q_e5))
+    q_col = list(q_q)
+    q_col[5] = mxq.MXQ_COLWISE
+    col_ms = time_calls(lambda: L.mxq_quantize(*q_col))
+    dq = torch.empty_like(qx)
+    dq_args = (qc.data_ptr(), qc.stride(0), qs.data_ptr(), qs.stride(0), mxq.MXQ_E4M3, qx.shape[0], qx.shape[1],
+               dq.data_ptr(), mxq.MXQ_BF16, dq.stride(0), sh)
+    L.mxq_quantize(*q_q)
+    dq_ms = time_calls(lambda: L.mxq_dequantize(*dq_args))
+    dq_bytes = qx.numel() * (1 + 1 / 32 + 2)
+    del qx, qc, qs, dq
 
     # quantize of the step's X alone (8192 x 4096 bf16)
     # X alone: 20 launches between two events (a single launch is short enough that the
@@ -221,6 +246,9 @@ def main():
                                  "frac_of_fp8_peak": round(exact_tflops / PEAK_MXFP8_TFLOPS, 4),
                                  "accum": "exact products, fp32 sums (bf16 matrix cores)"},
             "quantize_x": {"ms": round(xq_ms, 5), "gbs": round(xq_gbs, 1), "bytes": int(M * K * 3.03125)},
+            "quantize_2p28_e5m2": {"ms": round(e5_ms, 5), "gbs": round(q_bytes / (e5_ms * 1e-3) / 1e9, 1)},
+            "quantize_2p28_colwise": {"ms": round(col_ms, 5), "gbs": round(q_bytes / (col_ms * 1e-3) / 1e9, 1)},
+            "dequantize_2p28_bf16": {"ms": round(dq_ms, 5), "gbs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1)},
             "quantize_2p28": {"ms": round(q_ms, 5), "gbs": round(q_gbs, 1), "frac_hbm": round(q_gbs / PEAK_HBM_GBS, 4),
                               "bytes": int(q_bytes), "workload": "[16384][16384] bf16 Laplace(0,1) 1% x1e4, rowwise E4M3"},
         },

@@ -198,9 +198,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(const void* __restrict_
   }
 }
 
-// Columnwise: a workgroup stages a tile of 128 rows (4 blocks of K) x 64 columns in LDS,
-// then thread (c = tid % 64, kb = tid / 64) reduces and encodes the 32 values of block kb
-// of column c and writes its 32 codes (K-contiguous in the transposed output).
+// Columnwise: a workgroup stages a tile of 128 rows (4 blocks of K) x 64 columns in LDS
+// (row pitch padded by one dword, which spreads the column reads over the banks), then
+// thread t handles column t / 4, block t % 4: it reduces and encodes that block's 32
+// values and writes its 32 codes, so the 4 threads of a column write one contiguous
+// 128-byte run of the K-contiguous transposed output.
 constexpr int kColTileRows = 128;
 constexpr int kColTileCols = 64;
 
@@ -209,40 +211,51 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(const void* __restrict_
                                                         int64_t ld_src, int64_t nb, uint8_t* __restrict__ codes,
                                                         int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales) {
   typedef typename std::conditional<SRC_BF16, uint16_t, uint32_t>::type E;
-  __shared__ E tile[kColTileRows][kColTileCols];
+  constexpr int PW = kColTileCols * (int)sizeof(E) / 4 + 1;      // row pitch in dwords
+  __shared__ uint32_t tile[kColTileRows * PW];
   const int tid = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * kColTileCols;
   const E* s = reinterpret_cast<const E*>(src);
   for (int64_t ty = blockIdx.y; ty * kColTileRows < rows; ty += gridDim.y) {
     const int64_t r0 = ty * kColTileRows;
-    // stage: 16-byte pieces of each tile row
+    // stage: 16-byte pieces of each tile row, written to LDS as 4 dwords
     constexpr int EPV = 16 / sizeof(E);                 // elements per 16-byte piece
     constexpr int PPR = kColTileCols / EPV;             // pieces per tile row
     for (int p = tid; p < kColTileRows * PPR; p += kThreads) {
-      int tr = p / PPR, tc = (p % PPR) * EPV;
-      int64_t r = r0 + tr, cc = c0 + tc;
-      E* dst = &tile[tr][tc];
+      const int tr = p / PPR, tc = (p % PPR) * EPV;
+      const int64_t r = r0 + tr, cc = c0 + tc;
+      uint32_t* dst = &tile[tr * PW + tc * (int)sizeof(E) / 4];
       if (VEC && r < rows && cc + EPV <= cols) {
-        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(s + r * ld_src + cc);
+        const uint4 v = *reinterpret_cast<const uint4*>(s + r * ld_src + cc);
+        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
       } else {
+        E e[EPV];
 #pragma unroll
-        for (int i = 0; i < EPV; ++i) dst[i] = (r < rows && cc + i < cols) ? s[r * ld_src + cc + i] : (E)0;
+        for (int i = 0; i < EPV; ++i) e[i] = (r < rows && cc + i < cols) ? s[r * ld_src + cc + i] : (E)0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if (SRC_BF16) dst[w] = (uint32_t)e[2 * w] | ((uint32_t)e[2 * w + 1] << 16);
+          else dst[w] = (uint32_t)e[w];
+        }
       }
     }
     __syncthreads();
-    const int c = tid % kColTileCols, kb = tid / kColTileCols;
+    const int c = tid >> 2, kb = tid & 3;
     const int64_t col = c0 + c, b = r0 / 32 + kb;
     if (col < cols && b < nb) {
       uint32_t amax = 0;
       uint32_t v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        uint32_t x = tile[32 * kb + i][c];
-        v[i] = SRC_BF16 ? (x << 16) : x;
-        uint32_t a = v[i] & 0x7FFFFFFFu;
+        const int row = 32 * kb + i;
+        uint32_t x;
+        if (SRC_BF16) x = (uint32_t)reinterpret_cast<const uint16_t*>(tile)[row * PW * 2 + c] << 16;
+        else x = tile[row * PW + c];
+        v[i] = x;
+        const uint32_t a = x & 0x7FFFFFFFu;
         amax = amax > a ? amax : a;
       }
-      uint32_t sb = scale_byte_from_amax<F>(amax);
+      const uint32_t sb = scale_byte_from_amax<F>(amax);
       uint32_t out[8];
       if (sb == 255u) {
 #pragma unroll
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(const void* __restrict_
         const float scale = __uint_as_float(sb << 23);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          uint32_t w = cvt2_f32<F>(0u, v[4 * i], v[4 * i + 1], scale, false);
+          const uint32_t w = cvt2_f32<F>(0u, v[4 * i], v[4 * i + 1], scale, false);
           out[i] = cvt2_f32<F>(w, v[4 * i + 2], v[4 * i + 3], scale, true);
         }
       }
