@@ -118,6 +118,26 @@ int mxq_quantize(const void* src, int src_type, int64_t rows, int64_t cols, int6
                  int64_t ld_scales, void* stream);
 
 /*
+ * mxq_quantize_dual -- both orientations of one matrix from a single read of it.
+ * ("Microscaling: the two-row experiment", closing paragraph: moving from 1x32 to 32x1
+ * groups changes which values share a scale, so the second orientation is derived from
+ * the wide data, not by transposing the first one's bytes.)
+ *
+ * Equivalent to mxq_quantize(..., MXQ_ROWWISE, elem, row_codes, ...) followed by
+ * mxq_quantize(..., MXQ_COLWISE, elem, col_codes, ...) on the same src, bit for bit,
+ * with the same argument rules for each output:
+ *   row_codes [rows][ld_row_codes], ld >= 32*ceil(cols/32), row_scales [rows][>= ceil(cols/32)];
+ *   col_codes [cols][ld_col_codes], ld >= 32*ceil(rows/32), col_scales [cols][>= ceil(rows/32)].
+ * Code pointers 16-byte aligned, their leading dimensions multiples of 16.  One elem
+ * (MXQ_E4M3 or MXQ_E5M2) for both.  Reads src once: 4.0625 B per bf16 element instead of
+ * 2 x 3.03125 for the two separate calls.
+ */
+int mxq_quantize_dual(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int elem,
+                      uint8_t* row_codes, int64_t ld_row_codes, uint8_t* row_scales, int64_t ld_row_scales,
+                      uint8_t* col_codes, int64_t ld_col_codes, uint8_t* col_scales, int64_t ld_col_scales,
+                      void* stream);
+
+/*
  * mxq_dequantize -- reconstruction x_hat = dec(code) * 2^(s-127) (debug / fallback path).
  *
  * codes    [L][ld_codes] bytes (ld_codes >= K), scales [L][ld_scales] (ld_scales >= nb).

@@ -42,6 +42,8 @@ def lib():
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.mxq_quantize.restype = ci
         L.mxq_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, vp, i64, vp, i64, vp]
+        L.mxq_quantize_dual.restype = ci
+        L.mxq_quantize_dual.argtypes = [vp, ci, i64, i64, i64, ci, vp, i64, vp, i64, vp, i64, vp, i64, vp]
         L.mxq_dequantize.restype = ci
         L.mxq_dequantize.argtypes = [vp, i64, vp, i64, ci, i64, i64, vp, ci, i64, vp]
         L.mxq_gemm.restype = ci
@@ -61,6 +63,12 @@ def mxq_quantize(src, src_type, rows, cols, ld_src, axis, elem, codes, ld_codes,
                  stream=None) -> int:
     return lib().mxq_quantize(src, src_type, rows, cols, ld_src, axis, elem, codes, ld_codes, scales,
                               ld_scales, stream)
+
+
+def mxq_quantize_dual(src, src_type, rows, cols, ld_src, elem, row_codes, ld_row_codes, row_scales, ld_row_scales,
+                      col_codes, ld_col_codes, col_scales, ld_col_scales, stream=None) -> int:
+    return lib().mxq_quantize_dual(src, src_type, rows, cols, ld_src, elem, row_codes, ld_row_codes, row_scales,
+                                   ld_row_scales, col_codes, ld_col_codes, col_scales, ld_col_scales, stream)
 
 
 def mxq_dequantize(codes, ld_codes, scales, ld_scales, elem, L, K, dst, dst_type, ld_dst, stream=None) -> int:
@@ -141,6 +149,31 @@ def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None):
                       _stream_handle())
     _check(st, "mxq_quantize")
     return codes, scales
+
+
+def quantize_dual(x, elem: str = "e4m3"):
+    """Both MX orientations of a 2-D bf16/fp32 CUDA tensor from one read of it.
+
+    Returns (row_codes [rows][Kp_r], row_scales [rows][Kp_r/32], col_codes [cols][Kp_c],
+    col_scales [cols][Kp_c/32]) with K_r = cols and K_c = rows; identical to
+    quantize(x, elem, "row") and quantize(x, elem, "col").
+    """
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("quantize_dual expects a 2-D tensor")
+    if x.stride(1) != 1:
+        raise ValueError("quantize_dual expects unit stride along the last dimension")
+    rows, cols = x.shape
+    kp_r, kp_c = _round_up(cols, 32), _round_up(rows, 32)
+    rc = torch.empty((rows, kp_r), dtype=torch.uint8, device=x.device)
+    rs = torch.empty((rows, _round_up(kp_r // 32, 16)), dtype=torch.uint8, device=x.device)[:, :kp_r // 32]
+    cc = torch.empty((cols, kp_c), dtype=torch.uint8, device=x.device)
+    cs = torch.empty((cols, _round_up(kp_c // 32, 16)), dtype=torch.uint8, device=x.device)[:, :kp_c // 32]
+    st = mxq_quantize_dual(x.data_ptr(), _wide_type(x), rows, cols, x.stride(0) if rows > 0 else cols, _ELEM[elem],
+                           rc.data_ptr(), rc.stride(0), rs.data_ptr(), rs.stride(0), cc.data_ptr(), cc.stride(0),
+                           cs.data_ptr(), cs.stride(0), _stream_handle())
+    _check(st, "mxq_quantize_dual")
+    return rc, rs, cc, cs
 
 
 def dequantize(codes, scales, K: int, elem: str = "e4m3", out_dtype=None):

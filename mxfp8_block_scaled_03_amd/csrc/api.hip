@@ -70,6 +70,31 @@ int mxq_quantize(const void* src, int src_type, int64_t rows, int64_t cols, int6
                                            ld_codes, scales, ld_scales, src16, st));
 }
 
+int mxq_quantize_dual(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int elem,
+                      uint8_t* row_codes, int64_t ld_row_codes, uint8_t* row_scales, int64_t ld_row_scales,
+                      uint8_t* col_codes, int64_t ld_col_codes, uint8_t* col_scales, int64_t ld_col_scales,
+                      void* stream) {
+  if (!is_wide(src_type) || !is_elem(elem)) return MXQ_ERR_DTYPE;
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return MXQ_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MXQ_OK;
+  if (!src || !row_codes || !row_scales || !col_codes || !col_scales) return MXQ_ERR_NULL;
+  const int64_t kp_r = 32 * ((cols + 31) / 32), nb_r = kp_r / 32;
+  const int64_t kp_c = 32 * ((rows + 31) / 32), nb_c = kp_c / 32;
+  const int64_t es = src_type == MXQ_BF16 ? 2 : 4;
+  if (ld_src < cols || ld_row_codes < kp_r || ld_row_scales < nb_r || ld_col_codes < kp_c || ld_col_scales < nb_c)
+    return MXQ_ERR_LD;
+  if (!mul_ok(rows, ld_src * es) || !mul_ok(rows, ld_row_codes) || !mul_ok(rows, ld_row_scales) ||
+      !mul_ok(cols, ld_col_codes) || !mul_ok(cols, ld_col_scales))
+    return MXQ_ERR_SHAPE;
+  if (!aligned(src, (uintptr_t)es) || !aligned(row_codes, 16) || ld_row_codes % 16 != 0 || !aligned(col_codes, 16) ||
+      ld_col_codes % 16 != 0)
+    return MXQ_ERR_ALIGN;
+  const bool vec = aligned(src, 16) && (ld_src * es) % 16 == 0 && cols % 8 == 0;
+  return hip_status(mxq::launch_quant_dual(src, src_type == MXQ_BF16, rows, cols, ld_src, to_fmt(elem), row_codes,
+                                           ld_row_codes, row_scales, ld_row_scales, col_codes, ld_col_codes,
+                                           col_scales, ld_col_scales, vec, (hipStream_t)stream));
+}
+
 int mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales, int64_t ld_scales, int elem,
                    int64_t L, int64_t K, void* dst, int dst_type, int64_t ld_dst, void* stream) {
   if (!is_elem(elem) || !is_wide(dst_type)) return MXQ_ERR_DTYPE;

@@ -21,6 +21,12 @@ hipError_t launch_quant_cols(const void* src, int src_bf16, int64_t rows, int64_
                              int fmt, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
                              int64_t ld_scales, bool vec, hipStream_t stream);
 
+// Both orientations in one pass: rowwise codes [rows][ld_rc] (K = cols) and columnwise
+// codes [cols][ld_cc] (K = rows), with their scales.
+hipError_t launch_quant_dual(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, int fmt,
+                             uint8_t* rcodes, int64_t ld_rc, uint8_t* rscales, int64_t ld_rs, uint8_t* ccodes,
+                             int64_t ld_cc, uint8_t* cscales, int64_t ld_cs, bool vec, hipStream_t stream);
+
 hipError_t launch_dequant(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales, int64_t ld_scales,
                           int fmt, int64_t L, int64_t K, void* dst, int dst_bf16, int64_t ld_dst,
                           bool vec, hipStream_t stream);

@@ -26,6 +26,14 @@ typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 
+// Max over 32-bit patterns of the four lanes of a quad (quad_perm DPP: 1,0,3,2 then 2,3,0,1).
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  v = v > o ? v : o;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  return v > o ? v : o;
+}
+
 __device__ __forceinline__ uint32_t pk_abs_max_bf16(uint32_t acc, uint32_t w) {
   v2u16 a = __builtin_bit_cast(v2u16, acc);
   v2u16 b = __builtin_bit_cast(v2u16, w & 0x7FFF7FFFu);
@@ -285,6 +293,103 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(const void* __restrict_
   }
 }
 
+
+// Both orientations from one read ("Microscaling: the two-row experiment", last
+// paragraph: regrouping from 1x32 to 32x1 changes which values share a scale, so the
+// columnwise codes are derived from the wide data, not from the rowwise bytes).  A
+// workgroup takes a tile of 128 rows x 64 columns: thread t loads chunks (8 values) of
+// rows t/8 + 32k, chunk t%8, and the four lanes holding one 32-value row block reduce it
+// with DPP and write its rowwise codes and scale straight from registers; the tile also
+// goes to LDS, from which the columnwise blocks are encoded exactly as in k_quant_cols.
+template <int SRC_BF16, int F, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_quant_dual(const void* __restrict__ src, int64_t rows, int64_t cols,
+                                                        int64_t ld_src, uint8_t* __restrict__ rcodes, int64_t ld_rc,
+                                                        uint8_t* __restrict__ rscales, int64_t ld_rs,
+                                                        uint8_t* __restrict__ ccodes, int64_t ld_cc,
+                                                        uint8_t* __restrict__ cscales, int64_t ld_cs) {
+  typedef typename std::conditional<SRC_BF16, uint16_t, uint32_t>::type E;
+  constexpr int ES = (int)sizeof(E);
+  constexpr int PW = kColTileCols * ES / 4 + 1;      // LDS row pitch in dwords
+  __shared__ uint32_t tile[kColTileRows * PW];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kColTileCols;
+  const int64_t nb_r = (cols + 31) / 32, nb_c = (rows + 31) / 32;
+  const int64_t kp_r = 32 * nb_r;
+  const int tq = tid & 7;                             // chunk within the tile row
+  for (int64_t ty = blockIdx.y; ty * kColTileRows < rows; ty += gridDim.y) {
+    const int64_t r0 = ty * kColTileRows;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int tr = (tid >> 3) + 32 * k;
+      const int64_t r = r0 + tr;
+      const int64_t cc = c0 + 8 * tq;
+      Chunk<SRC_BF16> ch;
+      if (r < rows) {
+        const char* line = reinterpret_cast<const char*>(src) + r * ld_src * ES;
+        load_chunk<SRC_BF16, VEC>(ch, line, cc, cols);
+      } else {
+#pragma unroll
+        for (int i = 0; i < (SRC_BF16 ? 4 : 8); ++i) ch.w[i] = 0u;
+      }
+      // tile copy for the columnwise pass
+      uint32_t* dst = &tile[tr * PW + 8 * tq * ES / 4];
+#pragma unroll
+      for (int i = 0; i < (SRC_BF16 ? 4 : 8); ++i) dst[i] = ch.w[i];
+      // rowwise block of this quad (every lane of the wave takes part in the DPP)
+      const uint32_t amax = quad_max(chunk_abs_max<SRC_BF16>(ch));
+      const uint32_t sb = scale_byte_from_amax<F>(amax);
+      uint32_t d0, d1;
+      encode_chunk<SRC_BF16, F>(ch, sb, d0, d1);
+      if (r < rows && cc < kp_r) {
+        *reinterpret_cast<uint2*>(rcodes + r * ld_rc + cc) = make_uint2(d0, d1);
+        if ((tq & 3) == 0) rscales[r * ld_rs + (cc >> 5)] = (uint8_t)sb;
+      }
+    }
+    __syncthreads();
+    const int c = tid >> 2, kb = tid & 3;
+    const int64_t col = c0 + c, b = r0 / 32 + kb;
+    if (col < cols && b < nb_c) {
+      uint32_t amax = 0;
+      uint32_t v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int row = 32 * kb + i;
+        uint32_t x;
+        if (SRC_BF16) x = (uint32_t)reinterpret_cast<const uint16_t*>(tile)[row * PW * 2 + c] << 16;
+        else x = tile[row * PW + c];
+        v[i] = x;
+        const uint32_t a = x & 0x7FFFFFFFu;
+        amax = amax > a ? amax : a;
+      }
+      const uint32_t sb = scale_byte_from_amax<F>(amax);
+      uint32_t out[8];
+      if (sb == 255u) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = 0x7F7F7F7Fu;
+      } else if (sb == 0u) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w |= encode_rne_sat<F>(__uint_as_float(v[4 * i + j]) * 0x1p127f) << (8 * j);
+          out[i] = w;
+        }
+      } else {
+        const float scale = __uint_as_float(sb << 23);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t w = cvt2_f32<F>(0u, v[4 * i], v[4 * i + 1], scale, false);
+          out[i] = cvt2_f32<F>(w, v[4 * i + 2], v[4 * i + 3], scale, true);
+        }
+      }
+      uint4* dst = reinterpret_cast<uint4*>(ccodes + col * ld_cc + 32 * b);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      cscales[col * ld_cs + b] = (uint8_t)sb;
+    }
+    __syncthreads();
+  }
+}
 }  // namespace
 
 int device_cu_count() {
@@ -357,6 +462,36 @@ hipError_t launch_quant_cols(const void* src, int src_bf16, int64_t rows, int64_
   }
   if (fmt == kE4M3) return quant_cols_t<0, kE4M3>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
   return quant_cols_t<0, kE5M2>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+}
+
+template <int SRC_BF16, int F>
+static hipError_t quant_dual_t(const void* src, int64_t rows, int64_t cols, int64_t ld_src, uint8_t* rcodes,
+                               int64_t ld_rc, uint8_t* rscales, int64_t ld_rs, uint8_t* ccodes, int64_t ld_cc,
+                               uint8_t* cscales, int64_t ld_cs, bool vec, hipStream_t stream) {
+  const int64_t gx = (cols + kColTileCols - 1) / kColTileCols;
+  int64_t gy = (rows + kColTileRows - 1) / kColTileRows;
+  if (gy > 65535) gy = 65535;
+  if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (vec)
+    hipLaunchKernelGGL((k_quant_dual<SRC_BF16, F, true>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream,
+                       src, rows, cols, ld_src, rcodes, ld_rc, rscales, ld_rs, ccodes, ld_cc, cscales, ld_cs);
+  else
+    hipLaunchKernelGGL((k_quant_dual<SRC_BF16, F, false>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream,
+                       src, rows, cols, ld_src, rcodes, ld_rc, rscales, ld_rs, ccodes, ld_cc, cscales, ld_cs);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_dual(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, int fmt,
+                             uint8_t* rcodes, int64_t ld_rc, uint8_t* rscales, int64_t ld_rs, uint8_t* ccodes,
+                             int64_t ld_cc, uint8_t* cscales, int64_t ld_cs, bool vec, hipStream_t stream) {
+  if (src_bf16) {
+    if (fmt == kE4M3)
+      return quant_dual_t<1, kE4M3>(src, rows, cols, ld_src, rcodes, ld_rc, rscales, ld_rs, ccodes, ld_cc, cscales, ld_cs, vec, stream);
+    return quant_dual_t<1, kE5M2>(src, rows, cols, ld_src, rcodes, ld_rc, rscales, ld_rs, ccodes, ld_cc, cscales, ld_cs, vec, stream);
+  }
+  if (fmt == kE4M3)
+    return quant_dual_t<0, kE4M3>(src, rows, cols, ld_src, rcodes, ld_rc, rscales, ld_rs, ccodes, ld_cc, cscales, ld_cs, vec, stream);
+  return quant_dual_t<0, kE5M2>(src, rows, cols, ld_src, rcodes, ld_rc, rscales, ld_rs, ccodes, ld_cc, cscales, ld_cs, vec, stream);
 }
 
 }  // namespace mxq

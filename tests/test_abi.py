@@ -18,7 +18,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert {"mxq_quantize", "mxq_dequantize", "mxq_gemm", "mxq_status_string", "mxq_version"} <= set(declared_symbols())
+    assert {"mxq_quantize", "mxq_quantize_dual", "mxq_dequantize", "mxq_gemm", "mxq_status_string",
+            "mxq_version"} <= set(declared_symbols())
 
 
 def test_library_exports_every_declared_symbol():
@@ -67,6 +68,36 @@ def test_quantize_validation():
     # empty problems succeed without touching pointers
     assert q(rows=0, src=None, codes=None, scales=None) == 0
     assert q(cols=0, src=None, codes=None, scales=None) == 0
+
+
+def qd(**kw):
+    # rows = 40 -> column blocks Kp_c = 64; cols = 64 -> row blocks Kp_r = 64
+    a = dict(src=FAKE, src_type=mxq.MXQ_F32, rows=40, cols=64, ld_src=64, elem=mxq.MXQ_E5M2, rc=FAKE, ld_rc=64,
+             rs=FAKE, ld_rs=2, cc=FAKE, ld_cc=64, cs=FAKE, ld_cs=2)
+    a.update(kw)
+    return mxq.mxq_quantize_dual(a["src"], a["src_type"], a["rows"], a["cols"], a["ld_src"], a["elem"], a["rc"],
+                                 a["ld_rc"], a["rs"], a["ld_rs"], a["cc"], a["ld_cc"], a["cs"], a["ld_cs"], None)
+
+
+def test_quantize_dual_validation():
+    assert qd(src_type=mxq.MXQ_E4M3) == -5
+    assert qd(elem=mxq.MXQ_BF16) == -5
+    assert qd(rows=-1) == -2
+    assert qd(cols=1 << 40) == -2
+    for k in ("src", "rc", "rs", "cc", "cs"):
+        assert qd(**{k: None}) == -1
+    assert qd(ld_src=63) == -3
+    assert qd(ld_rc=48) == -3                # < Kp_r = 64
+    assert qd(ld_rs=1) == -3
+    assert qd(ld_cc=48) == -3                # < Kp_c = 64
+    assert qd(ld_cs=1) == -3
+    assert qd(ld_rc=72) == -4                # not a multiple of 16
+    assert qd(ld_cc=72) == -4
+    assert qd(rc=FAKE + 8) == -4
+    assert qd(cc=FAKE + 4) == -4
+    assert qd(src=FAKE + 2) == -4            # fp32 needs 4-byte alignment
+    assert qd(rows=0, src=None, rc=None, rs=None, cc=None, cs=None) == 0
+    assert qd(cols=0, src=None, rc=None, rs=None, cc=None, cs=None) == 0
 
 
 def g(**kw):

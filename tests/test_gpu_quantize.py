@@ -211,6 +211,113 @@ def test_standalone_quantize_2p28():
         del gc, gs, oc, os_
 
 
+# ----------------------------------------------------------------- both orientations at once
+
+def gpu_quantize_dual(x_cpu: torch.Tensor, fmt: str, pad=16, x_dev=None):
+    """mxq_quantize_dual into canary-filled, over-wide outputs; checks the canaries and
+    returns (row codes, row scales, col codes, col scales) trimmed to Kp and nb."""
+    rows, cols = x_cpu.shape
+    kr, kc = 32 * ((cols + 31) // 32), 32 * ((rows + 31) // 32)
+    bufs = [torch.full(shape, 0xCD, dtype=torch.uint8, device=DEV)
+            for shape in ((rows, kr + pad), (rows, kr // 32 + 3), (cols, kc + pad), (cols, kc // 32 + 3))]
+    x = x_cpu.to(DEV) if x_dev is None else x_dev
+    st = mxq.mxq_quantize_dual(x.data_ptr(), mxq._binding._wide_type(x), rows, cols, x.stride(0), mxq._binding._ELEM[fmt],
+                               *[v for b in bufs for v in (b.data_ptr(), b.stride(0))],
+                               mxq._binding._stream_handle())
+    assert st == 0, mxq.mxq_status_string(st)
+    torch.cuda.synchronize()
+    rc, rs, cc, cs = (b.cpu().numpy() for b in bufs)
+    assert np.all(rc[:, kr:] == 0xCD) and np.all(rs[:, kr // 32:] == 0xCD), "rowwise write past the end"
+    assert np.all(cc[:, kc:] == 0xCD) and np.all(cs[:, kc // 32:] == 0xCD), "columnwise write past the end"
+    return rc[:, :kr], rs[:, :kr // 32], cc[:, :kc], cs[:, :kc // 32]
+
+
+def check_dual(x_cpu, fmt, what, **kw):
+    rc, rs, cc, cs = gpu_quantize_dual(x_cpu, fmt, **kw)
+    oc, os_ = oracle_quantize(x_cpu, fmt, "row")
+    assert_same(rc, rs, oc, os_, what + " rowwise")
+    oc, os_ = oracle_quantize(x_cpu, fmt, "col")
+    assert_same(cc, cs, oc, os_, what + " columnwise")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quantize_dual_shapes(dtype, fmt):
+    """Ragged in both directions (partial 32-blocks, partial 128x64 tiles), tiny and
+    several-tile shapes, column counts that do and do not allow 16-byte loads."""
+    rng = np.random.default_rng(20)
+    for rows, cols in SHAPES + [(128, 64), (129, 65), (300, 136), (257, 1000), (1000, 48)]:
+        say("dual %s %s %dx%d" % (dtype, fmt, rows, cols))
+        scale = np.exp2(rng.integers(-20, 20, (rows, 1))).astype(np.float32)
+        x = torch.from_numpy(rng.standard_normal((rows, cols)).astype(np.float32) * scale).to(dtype)
+        check_dual(x, fmt, "%dx%d" % (rows, cols))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_quantize_dual_special_values(dtype, fmt):
+    """The special-value rows of test_quantize_special_values, which also put NaN, Inf,
+    zero and tiny columns into the columnwise blocks."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((96, 256)).astype(np.float32)
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2, :32] = np.nan
+    x[2, 40] = np.inf
+    x[3, 70] = -np.inf
+    x[4] = rng.standard_normal(256).astype(np.float32) * 1e-38
+    x[5] = rng.standard_normal(256).astype(np.float32) * 1e-40
+    x[6, :] = 2.0 ** -133
+    x[7] = rng.standard_normal(256).astype(np.float32) * 3e38
+    x[8, ::7] = 500.0
+    x[10] = (rng.integers(-16, 16, 256) * 2.0 ** -4).astype(np.float32)
+    x[32:64, 100:132] = 1e-39                                            # a tiny columnwise block
+    x[64:96, 200] = np.nan
+    check_dual(torch.from_numpy(x).to(dtype), fmt, "special")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_dual_strided_and_unaligned(dtype):
+    """Views whose leading dimension is not the row length, starting one element into the
+    allocation (the path with element loads)."""
+    rng = np.random.default_rng(22)
+    base = torch.from_numpy(rng.standard_normal((170, 101)).astype(np.float32)).to(dtype)
+    gpu_base = base.to(DEV)
+    for r0, c0, rows, cols in ((0, 1, 170, 96), (3, 0, 140, 64), (1, 5, 130, 33)):
+        say("dual view %d,%d %dx%d" % (r0, c0, rows, cols))
+        view = base[r0:r0 + rows, c0:c0 + cols]
+        check_dual(view.contiguous(), "e4m3", "view", x_dev=gpu_base[r0:r0 + rows, c0:c0 + cols])
+
+
+def test_quantize_dual_matches_separate_calls_2p28():
+    """The 2^28-element bf16 tensor: the fused call gives the same bytes as the rowwise and
+    columnwise calls (which are checked against the oracle in test_standalone_quantize_2p28),
+    so the fused kernel is pinned to the oracle at full size too."""
+    d = wl.workload_q()
+    x = d["x"].to(DEV)
+    for fmt in ("e4m3", "e5m2"):
+        say("dual 2^28 %s" % fmt)
+        rc, rs, cc, cs = mxq.quantize_dual(x, fmt)
+        c, s = mxq.quantize(x, fmt, "row")
+        assert torch.equal(rc, c) and torch.equal(rs, s)
+        c, s = mxq.quantize(x, fmt, "col")
+        assert torch.equal(cc, c) and torch.equal(cs, s)
+        del rc, rs, cc, cs, c, s
+
+
+def test_workload4_quantize_dual():
+    """The backward gradient dY in e5m2, both orientations, against the oracle."""
+    d = wl.workload4()
+    say("workload4 dual dY")
+    check_dual(d["dy"], "e5m2", "dY", pad=0)
+
+
+def test_quantize_dual_empty_is_a_no_op():
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    rc, rs, cc, cs = mxq.quantize_dual(x)
+    assert rc.shape == (0, 64) and cc.shape == (64, 0)
+
+
 # ----------------------------------------------------------------- dequantize
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
