@@ -182,6 +182,44 @@ int mxq_gemm(int64_t M, int64_t N, int64_t K,
              const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws, int w_elem,
              float alpha, const float* bias, void* y, int y_type, int64_t ld_y, int accum, void* stream);
 
+/*
+ * Activation applied in the GEMM epilogue ("Hardware support and kernel ABI contracts":
+ * the kernel contract's epilogue names an FP32 bias, a SiLU activation and the output
+ * dtype; "Scale ownership and the GEMM dataflow": the epilogue may pipe the result into
+ * a fused bias and activation).
+ * MXQ_ACT_SILU  silu(v) = v / (1 + e^-v), evaluated in FP32 as v / (1 + t) for v >= 0 and
+ *               v * t / (1 + t) for v < 0 with t = e^-|v| (no intermediate overflows;
+ *               within 8 FP32 ulp of the exact value, plus 2^-126 absolute below).
+ */
+typedef enum { MXQ_ACT_NONE = 0, MXQ_ACT_SILU = 1 } mxq_act;
+
+/*
+ * mxq_gemm_ex -- mxq_gemm with an activation and a producer-fused quantized output.
+ * ("Scale ownership and the GEMM dataflow": a preceding epilogue can itself produce the
+ * codes and scales the next GEMM consumes -- producer fusion -- instead of a separate
+ * conversion kernel reading the wide tensor back.)
+ *
+ * Operands, accum, alpha, bias and limits as for mxq_gemm.  Per output element
+ *   v = act(alpha * acc + bias[j])          (FP32; act = MXQ_ACT_NONE or MXQ_ACT_SILU)
+ * y        [M][ld_y] of y_type (F32 or BF16, RNE) receives v, as in mxq_gemm; may be NULL.
+ * q_codes  [M][ld_q_codes] and q_scales [M][ld_q_scales] (may be NULL together) receive
+ *          the MX quantization of bf16(v) along each row, 32-column blocks, element
+ *          format q_elem (MXQ_E4M3 / MXQ_E5M2): byte for byte what
+ *          mxq_quantize(Y_bf16, MXQ_ROWWISE, q_elem) gives for the bf16 Y this call
+ *          writes with y_type = MXQ_BF16 -- i.e. rows ready to be the X operand of the
+ *          next GEMM (K' = N).  ld_q_codes >= Np = 32*ceil(N/32) and a multiple of 16,
+ *          q_codes 16-byte aligned, ld_q_scales >= Np/32; codes of columns N..Np-1 are 0.
+ * At least one of y and q_codes must be given (MXQ_ERR_NULL otherwise).  Writing only
+ * the codes saves the wide output's write and the quantize pass's read of it.
+ */
+int mxq_gemm_ex(int64_t M, int64_t N, int64_t K,
+                const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_elem,
+                const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws, int w_elem,
+                float alpha, const float* bias, int act,
+                void* y, int y_type, int64_t ld_y,
+                int q_elem, uint8_t* q_codes, int64_t ld_q_codes, uint8_t* q_scales, int64_t ld_q_scales,
+                int accum, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* mxq_status_string(int status);
 

@@ -10,9 +10,11 @@ _LIB_PATH = os.path.join(PKG, "libmxq.so")
 MXQ_F32, MXQ_BF16, MXQ_E4M3, MXQ_E5M2 = 0, 1, 2, 3
 MXQ_ROWWISE, MXQ_COLWISE = 0, 1
 MXQ_ACC_FP8_MFMA, MXQ_ACC_FP32 = 0, 1
+MXQ_ACT_NONE, MXQ_ACT_SILU = 0, 1
 
 _ELEM = {"e4m3": MXQ_E4M3, "e5m2": MXQ_E5M2}
 _ACC = {"fp8": MXQ_ACC_FP8_MFMA, "fp32": MXQ_ACC_FP32}
+_ACT = {None: MXQ_ACT_NONE, "none": MXQ_ACT_NONE, "silu": MXQ_ACT_SILU}
 _AXIS = {"row": MXQ_ROWWISE, "col": MXQ_COLWISE, 0: MXQ_ROWWISE, 1: MXQ_COLWISE}
 
 
@@ -49,6 +51,9 @@ def lib():
         L.mxq_gemm.restype = ci
         L.mxq_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, ci, vp, i64, vp, i64, ci,
                                ctypes.c_float, vp, vp, ci, i64, ci, vp]
+        L.mxq_gemm_ex.restype = ci
+        L.mxq_gemm_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, ci, vp, i64, vp, i64, ci,
+                                  ctypes.c_float, vp, ci, vp, ci, i64, ci, vp, i64, vp, i64, ci, vp]
         L.mxq_status_string.restype = ctypes.c_char_p
         L.mxq_status_string.argtypes = [ci]
         L.mxq_version.restype = ci
@@ -79,6 +84,14 @@ def mxq_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_s
              alpha, bias, y, y_type, ld_y, accum=MXQ_ACC_FP8_MFMA, stream=None) -> int:
     return lib().mxq_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws,
                           w_elem, alpha, bias, y, y_type, ld_y, accum, stream)
+
+
+def mxq_gemm_ex(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws, w_elem,
+                alpha, bias, act, y, y_type, ld_y, q_elem, q_codes, ld_q_codes, q_scales, ld_q_scales,
+                accum=MXQ_ACC_FP8_MFMA, stream=None) -> int:
+    return lib().mxq_gemm_ex(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws,
+                             w_elem, alpha, bias, act, y, y_type, ld_y, q_elem, q_codes, ld_q_codes, q_scales,
+                             ld_q_scales, accum, stream)
 
 
 def mxq_status_string(status: int) -> str:
@@ -189,19 +202,40 @@ def dequantize(codes, scales, K: int, elem: str = "e4m3", out_dtype=None):
 
 
 def gemm(x_codes, x_scales, w_codes, w_scales, K: int, x_elem: str = "e4m3", w_elem: str = "e4m3",
-         alpha: float = 1.0, bias=None, out_dtype=None, out=None, accum: str = "fp8"):
-    """Y[M][N] = alpha * (X W) + bias with X = (x_codes [M][Kp], x_scales) and W column-major
+         alpha: float = 1.0, bias=None, out_dtype=None, out=None, accum: str = "fp8", act=None,
+         quant_out=None, wide_out: bool = True):
+    """Y[M][N] = act(alpha * (X W) + bias) with X = (x_codes [M][Kp], x_scales) and W column-major
     (w_codes [N][Kp], w_scales).  accum="fp8": FP8 matrix cores (fast); accum="fp32":
-    exact products summed in FP32 (see mxq_accum in include/mxq.h)."""
+    exact products summed in FP32 (see mxq_accum in include/mxq.h).  act: None or "silu".
+
+    quant_out="e4m3"/"e5m2" also returns the MX codes [M][Np] and scales of bf16(Y) along
+    N, produced in the GEMM's epilogue (byte for byte quantize(Y_bf16, elem, "row"));
+    wide_out=False then skips writing Y.  Returns Y, or (Y or None, codes, scales)."""
     torch = _torch()
     M, N = x_codes.shape[0], w_codes.shape[0]
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=x_codes.device)
     if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N):
         raise ValueError("bias must be a float32 tensor of N elements")
-    st = mxq_gemm(M, N, K, x_codes.data_ptr(), x_codes.stride(0), x_scales.data_ptr(), x_scales.stride(0),
-                  _ELEM[x_elem], w_codes.data_ptr(), w_codes.stride(0), w_scales.data_ptr(), w_scales.stride(0),
-                  _ELEM[w_elem], float(alpha), None if bias is None else bias.data_ptr(), out.data_ptr(),
-                  _wide_type(out), out.stride(0), _ACC[accum], _stream_handle())
-    _check(st, "mxq_gemm")
-    return out
+    if act not in _ACT:
+        raise ValueError("act must be None or 'silu'")
+    if quant_out is None and not wide_out:
+        raise ValueError("nothing to write: wide_out=False needs quant_out")
+    if wide_out and out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=x_codes.device)
+    y = out if wide_out else None
+    qc = qs = None
+    if quant_out is not None:
+        np_ = _round_up(N, 32)
+        qc = torch.empty((M, np_), dtype=torch.uint8, device=x_codes.device)
+        qs = torch.empty((M, _round_up(np_ // 32, 16)), dtype=torch.uint8, device=x_codes.device)[:, :np_ // 32]
+    st = mxq_gemm_ex(M, N, K, x_codes.data_ptr(), x_codes.stride(0), x_scales.data_ptr(), x_scales.stride(0),
+                     _ELEM[x_elem], w_codes.data_ptr(), w_codes.stride(0), w_scales.data_ptr(), w_scales.stride(0),
+                     _ELEM[w_elem], float(alpha), None if bias is None else bias.data_ptr(), _ACT[act],
+                     None if y is None else y.data_ptr(), MXQ_BF16 if y is None else _wide_type(y),
+                     0 if y is None else y.stride(0), _ELEM[quant_out or "e4m3"],
+                     None if qc is None else qc.data_ptr(), 0 if qc is None else qc.stride(0),
+                     None if qs is None else qs.data_ptr(), 0 if qs is None else qs.stride(0),
+                     _ACC[accum], _stream_handle())
+    _check(st, "mxq_gemm_ex")
+    if quant_out is None:
+        return y
+    return y, qc, qs

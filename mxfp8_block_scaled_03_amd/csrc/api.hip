@@ -111,19 +111,23 @@ int mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales
                                         dst_type == MXQ_BF16, ld_dst, vec, (hipStream_t)stream));
 }
 
-int mxq_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales,
-             int64_t ld_xs, int x_elem, const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws,
-             int w_elem, float alpha, const float* bias, void* y, int y_type, int64_t ld_y, int accum, void* stream) {
-  if (!is_elem(x_elem) || !is_elem(w_elem) || !is_wide(y_type)) return MXQ_ERR_DTYPE;
+int mxq_gemm_ex(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales,
+                int64_t ld_xs, int x_elem, const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales,
+                int64_t ld_ws, int w_elem, float alpha, const float* bias, int act, void* y, int y_type,
+                int64_t ld_y, int q_elem, uint8_t* q_codes, int64_t ld_q_codes, uint8_t* q_scales,
+                int64_t ld_q_scales, int accum, void* stream) {
+  if (!is_elem(x_elem) || !is_elem(w_elem)) return MXQ_ERR_DTYPE;
+  if (y && !is_wide(y_type)) return MXQ_ERR_DTYPE;
+  if (q_codes && !is_elem(q_elem)) return MXQ_ERR_DTYPE;
   if (accum != MXQ_ACC_FP8_MFMA && accum != MXQ_ACC_FP32) return MXQ_ERR_ARG;
+  if (act != MXQ_ACT_NONE && act != MXQ_ACT_SILU) return MXQ_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxCodeLd) return MXQ_ERR_SHAPE;
   if (!isfinite(alpha)) return MXQ_ERR_ARG;
   if (M == 0 || N == 0) return MXQ_OK;
   const int64_t Kp = 32 * ((K + 31) / 32), nb = Kp / 32;
-  if (!y) return MXQ_ERR_NULL;
+  if (!y && !q_codes) return MXQ_ERR_NULL;
+  if (q_codes && !q_scales) return MXQ_ERR_NULL;
   if (K > 0 && (!x_codes || !x_scales || !w_codes || !w_scales)) return MXQ_ERR_NULL;
-  const int64_t ey = y_type == MXQ_BF16 ? 2 : 4;
-  if (ld_y < N) return MXQ_ERR_LD;
   if (K > 0) {
     if (ld_x < Kp || ld_w < Kp || ld_xs < nb || ld_ws < nb) return MXQ_ERR_LD;
     if (ld_x >= kMaxCodeLd || ld_w >= kMaxCodeLd || ld_xs >= kMaxCodeLd / 2 || ld_ws >= kMaxCodeLd / 2)
@@ -131,11 +135,49 @@ int mxq_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld
     if (!aligned(x_codes, 16) || !aligned(w_codes, 16) || ld_x % 16 != 0 || ld_w % 16 != 0) return MXQ_ERR_ALIGN;
     if (!mul_ok(M, ld_x) || !mul_ok(N, ld_w) || !mul_ok(M, ld_xs) || !mul_ok(N, ld_ws)) return MXQ_ERR_SHAPE;
   }
-  if (!mul_ok(M, ld_y * ey)) return MXQ_ERR_SHAPE;
-  if (!aligned(y, (uintptr_t)ey) || (bias && !aligned(bias, 4))) return MXQ_ERR_ALIGN;
+  const int64_t ey = y_type == MXQ_BF16 ? 2 : 4;
+  if (y) {
+    if (ld_y < N) return MXQ_ERR_LD;
+    if (!mul_ok(M, ld_y * ey)) return MXQ_ERR_SHAPE;
+    if (!aligned(y, (uintptr_t)ey)) return MXQ_ERR_ALIGN;
+  }
+  if (q_codes) {
+    const int64_t np = 32 * ((N + 31) / 32);
+    if (ld_q_codes < np || ld_q_scales < np / 32) return MXQ_ERR_LD;
+    if (!mul_ok(M, ld_q_codes) || !mul_ok(M, ld_q_scales)) return MXQ_ERR_SHAPE;
+    if (!aligned(q_codes, 16) || ld_q_codes % 16 != 0) return MXQ_ERR_ALIGN;
+  }
+  if (bias && !aligned(bias, 4)) return MXQ_ERR_ALIGN;
+  mxq::GemmEpilogue ep{};
+  ep.alpha = alpha;
+  ep.bias = bias;
+  ep.act = act == MXQ_ACT_SILU ? 1 : 0;
+  ep.y = y;
+  ep.y_bf16 = y ? (y_type == MXQ_BF16) : 1;
+  ep.ld_y = y ? ld_y : 0;
+  ep.qc = q_codes;
+  ep.ld_qc = q_codes ? ld_q_codes : 0;
+  ep.qs = q_codes ? q_scales : nullptr;
+  ep.ld_qs = q_codes ? ld_q_scales : 0;
+  ep.q_fmt = q_codes ? to_fmt(q_elem) : 0;
   return hip_status(mxq::launch_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, to_fmt(x_elem), w_codes, ld_w, w_scales,
-                                     ld_ws, to_fmt(w_elem), alpha, bias, y, y_type == MXQ_BF16, ld_y,
-                                     accum == MXQ_ACC_FP32, (hipStream_t)stream));
+                                     ld_ws, to_fmt(w_elem), ep, accum == MXQ_ACC_FP32, (hipStream_t)stream));
+}
+
+int mxq_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales,
+             int64_t ld_xs, int x_elem, const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws,
+             int w_elem, float alpha, const float* bias, void* y, int y_type, int64_t ld_y, int accum, void* stream) {
+  if (!is_wide(y_type)) return MXQ_ERR_DTYPE;
+  if (!y && M > 0 && N > 0 && M < kMaxDim && N < kMaxDim) {
+    // the wide output is required here (mxq_gemm_ex also accepts a quantized one instead)
+    if (!is_elem(x_elem) || !is_elem(w_elem)) return MXQ_ERR_DTYPE;
+    if (accum != MXQ_ACC_FP8_MFMA && accum != MXQ_ACC_FP32) return MXQ_ERR_ARG;
+    if (K < 0 || K >= kMaxCodeLd) return MXQ_ERR_SHAPE;
+    if (!isfinite(alpha)) return MXQ_ERR_ARG;
+    return MXQ_ERR_NULL;
+  }
+  return mxq_gemm_ex(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws, w_elem, alpha,
+                     bias, MXQ_ACT_NONE, y, y_type, ld_y, MXQ_E4M3, nullptr, 0, nullptr, 0, accum, stream);
 }
 
 }  // extern "C"

@@ -28,6 +28,7 @@
 
 #include "codec.hpp"
 #include "internal.hpp"
+#include "mxblock.hpp"
 
 namespace mxq {
 namespace {
@@ -57,6 +58,61 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // (folded into the ds_read_b128 immediate).
 __device__ __forceinline__ v4i lds16(uint32_t addr, int off) {
   return *reinterpret_cast<const v4i*>(smem + addr + off);
+}
+
+// SiLU, x * sigmoid(x), in fp32 without an overflowing intermediate: with t = e^-|x|,
+// x / (1 + t) for x >= 0 and x * t / (1 + t) for x < 0.
+__device__ __forceinline__ float silu(float x) {
+  const float t = expf(-fabsf(x));
+  return x >= 0.0f ? x / (1.0f + t) : x * t / (1.0f + t);
+}
+
+
+// MX-quantize a wave's block of bf16 output values staged in LDS, along its rows: 128 rows
+// of 32 * NB values at LDS offset `base`, row pitch 64 * NB bytes, 16-byte chunk c of row r
+// stored at chunk c ^ (r & 7), values past column N staged as +0 (the zero padding of a
+// partial block).  Row r, block j becomes block blk0 + j of code row row0 + r ("Microscaling:
+// the two-row experiment": amax, power-of-two scale, RNE codes), written only when the row
+// is < M and the block < nbq.
+template <int NB>
+__device__ __forceinline__ void quantize_staged(uint32_t base, int lane, int row0, int M, int blk0, int nbq,
+                                                const GemmEpilogue& ep) {
+  constexpr int PITCH = 64 * NB;
+#pragma unroll 1
+  for (int it = 0; it < 2 * NB; ++it) {
+    const int p = 64 * it + lane, r = p / NB, j = p % NB;
+    mxblock::Chunk<1> ch[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t phys = (uint32_t)((4 * j + c) ^ (r & 7));
+      const v4i v = lds16(base + (uint32_t)(r * PITCH) + (phys << 4), 0);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) ch[c].w[w] = (uint32_t)v[w];
+    }
+    const int row = row0 + r, b = blk0 + j;
+    if (row < M && b < nbq) {
+      uint32_t amax = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t a = mxblock::chunk_abs_max<1>(ch[c]);
+        amax = amax > a ? amax : a;
+      }
+      uint32_t d[8], sb;
+      if (ep.q_fmt == kE4M3) {
+        sb = scale_byte_from_amax<kE4M3>(amax);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mxblock::encode_chunk<1, kE4M3>(ch[c], sb, d[2 * c], d[2 * c + 1]);
+      } else {
+        sb = scale_byte_from_amax<kE5M2>(amax);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mxblock::encode_chunk<1, kE5M2>(ch[c], sb, d[2 * c], d[2 * c + 1]);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(ep.qc + (int64_t)row * ep.ld_qc + 32 * (int64_t)b);
+      dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
+      dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
+      ep.qs[(int64_t)row * ep.ld_qs + b] = (uint8_t)sb;
+    }
+  }
 }
 
 // Keep the first `lim` bytes of a 16-byte fragment half, zero the rest.
@@ -213,14 +269,13 @@ __device__ __forceinline__ void mask_tail(uint32_t so, int krem) {
   }
 }
 
-template <int MODE, int FA, int FB, int Y_BF16, bool BIAS>
+template <int MODE, int FA, int FB>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(int M, int N, int K, int tiles_m, int tiles_n,
                                                      const uint8_t* __restrict__ xc, int64_t ld_x,
                                                      const uint8_t* __restrict__ xs, int64_t ld_xs,
                                                      const uint8_t* __restrict__ wc, int64_t ld_w,
-                                                     const uint8_t* __restrict__ ws, int64_t ld_ws, float alpha,
-                                                     const float* __restrict__ bias, void* __restrict__ y,
-                                                     int64_t ld_y) {
+                                                     const uint8_t* __restrict__ ws, int64_t ld_ws,
+                                                     const GemmEpilogue ep) {
   // ---- tile selection: XCD-first, then grouped rows
   const int ntiles = tiles_m * tiles_n;
   const int wg = blockIdx.x;
@@ -350,25 +405,73 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(int M, int N, int K, int t
     for (int f = 0; f < 4; ++f) { sa[f] = na[f]; sb[f] = nbx[f]; }
   }
 
-  // ---- epilogue: y = alpha * acc + bias[col], rounded once to the output type
+  // ---- epilogue: v = act(alpha * acc + bias[col]) in place (lane (g, i) holds column
+  //      32 fj + i, row 32 fi + 8 (r / 4) + 4 g + r % 4 of the wave's 128x128 block); y = v
+  //      rounded once to its type; the MX codes of bf16(v) along rows
+  {
+    const bool has_bias = ep.bias != nullptr;
 #pragma unroll
-  for (int fj = 0; fj < 4; ++fj) {
-    const int col = n0 + wn * 128 + 32 * fj + li;
-    const float bv = (BIAS && col < N) ? bias[col] : 0.0f;
+    for (int fj = 0; fj < 4; ++fj) {
+      const int col = n0 + wn * 128 + 32 * fj + li;
+      const float bv = (has_bias && col < N) ? ep.bias[col] : 0.0f;
 #pragma unroll
-    for (int fi = 0; fi < 4; ++fi) {
+      for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + 32 * fi + 8 * (r >> 2) + 4 * lg + (r & 3);
-        if (row < M && col < N) {
-          const float v = BIAS ? __builtin_fmaf(alpha, acc[fi][fj][r], bv) : alpha * acc[fi][fj][r];
-          if (Y_BF16)
-            reinterpret_cast<uint16_t*>(y)[(int64_t)row * ld_y + col] = (uint16_t)f32_to_bf16_rne(v);
-          else
-            reinterpret_cast<float*>(y)[(int64_t)row * ld_y + col] = v;
+        for (int r = 0; r < 16; ++r)
+          acc[fi][fj][r] = has_bias ? __builtin_fmaf(ep.alpha, acc[fi][fj][r], bv) : ep.alpha * acc[fi][fj][r];
+    }
+    if (ep.act) {
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = silu(acc[fi][fj][r]);
+    }
+  }
+  if (ep.y) {
+#pragma unroll
+    for (int fj = 0; fj < 4; ++fj) {
+      const int col = n0 + wn * 128 + 32 * fj + li;
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 128 + 32 * fi + 8 * (r >> 2) + 4 * lg + (r & 3);
+          if (row < M && col < N) {
+            if (ep.y_bf16)
+              reinterpret_cast<uint16_t*>(ep.y)[(int64_t)row * ep.ld_y + col] =
+                  (uint16_t)f32_to_bf16_rne(acc[fi][fj][r]);
+            else
+              reinterpret_cast<float*>(ep.y)[(int64_t)row * ep.ld_y + col] = acc[fi][fj][r];
+          }
         }
       }
     }
+  }
+  if (ep.qc) {
+    // the loop's last barrier has retired every LDS read and DMA of the main loop; each
+    // wave stages bf16(v) of its block in its own 32 KiB, columns >= N as +0
+    const uint32_t wbase = (uint32_t)wid * 32768u;
+#pragma unroll
+    for (int fj = 0; fj < 4; ++fj) {
+      const int cw = 32 * fj + li;
+      const bool in = n0 + wn * 128 + cw < N;
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rw = 32 * fi + 8 * (r >> 2) + 4 * lg + (r & 3);
+          const uint32_t addr = wbase + (uint32_t)(rw * 256) + ((uint32_t)((cw >> 3) ^ (rw & 7)) << 4) +
+                                (uint32_t)((2 * cw) & 15);
+          *reinterpret_cast<uint16_t*>(smem + addr) = in ? (uint16_t)f32_to_bf16_rne(acc[fi][fj][r]) : (uint16_t)0;
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    quantize_staged<4>(wbase, lane, m0 + wm * 128, M, (n0 + wn * 128) / 32, (N + 31) / 32, ep);
   }
 }
 
@@ -523,14 +626,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
 }
 
-template <int FA, int FB, int Y_BF16, bool BIAS>
+template <int FA, int FB>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, int tiles_m, int tiles_n,
                                                         const uint8_t* __restrict__ xc, int64_t ld_x,
                                                         const uint8_t* __restrict__ xs, int64_t ld_xs,
                                                         const uint8_t* __restrict__ wc, int64_t ld_w,
-                                                        const uint8_t* __restrict__ ws, int64_t ld_ws, float alpha,
-                                                        const float* __restrict__ bias, void* __restrict__ y,
-                                                        int64_t ld_y, int y_vec16) {
+                                                        const uint8_t* __restrict__ ws, int64_t ld_ws,
+                                                        const GemmEpilogue ep) {
   // ---- tile selection: XCD-first, then grouped rows
   const int ntiles = tiles_m * tiles_n;
   const int wg = blockIdx.x;
@@ -748,17 +850,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
   }
   if (gp == 0) lds_barrier();   // matches group 1's extra barrier: all LDS reads are done
 
-  // ---- epilogue: y = alpha * acc + bias[col], rounded once to the output type.  Lane
-  //      (g, i) holds Y[row 32 fi + i][col 32 fj + 8 q + 4 g + e] in acc[fi][fj][4 q + e]
-  //      (rows and columns relative to the wave's 128x64 block).
+  // ---- epilogue: v = act(alpha * acc + bias[col]) in place; y = v rounded once to its
+  //      type; the MX codes of bf16(v) along rows.  Lane (g, i) holds Y[row 32 fi + i][col
+  //      32 fj + 8 q + 4 g + e] in acc[fi][fj][4 q + e] (rows and columns relative to the
+  //      wave's 128x64 block).
   const int wrow0 = m0 + gp * 128, wcol0 = n0 + wq * 64;
-  auto value = [&](int fi, int fj, int r, float bv) {
-    return BIAS ? __builtin_fmaf(alpha, acc[fi][fj][r], bv) : alpha * acc[fi][fj][r];
-  };
-  if (y_vec16 && m0 + BM <= M && n0 + BN <= N) {
-    // stage the block in this wave's LDS region as row-major rows of 64 values with the
-    // 16-byte chunk index XOR (row & 7), then store whole 16-byte row pieces
-    constexpr int E = Y_BF16 ? 2 : 4;                // bytes per value
+  {
+    const bool has_bias = ep.bias != nullptr;
+#pragma unroll
+    for (int fj = 0; fj < 2; ++fj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = wcol0 + 32 * fj + 8 * q + 4 * lg + e;
+          const float bv = (has_bias && col < N) ? ep.bias[col] : 0.0f;
+#pragma unroll
+          for (int fi = 0; fi < 4; ++fi) {
+            const float a = acc[fi][fj][4 * q + e];
+            acc[fi][fj][4 * q + e] = has_bias ? __builtin_fmaf(ep.alpha, a, bv) : ep.alpha * a;
+          }
+        }
+    if (ep.act) {
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < 2; ++fj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = silu(acc[fi][fj][r]);
+    }
+  }
+  // interior tile, aligned y: stage the block in this wave's LDS region as row-major rows
+  // of 64 values with the 16-byte chunk index XOR (row & 7), then store whole 16-byte row
+  // pieces (E = bytes per value)
+  auto store_staged = [&](auto e_c) {
+    constexpr int E = decltype(e_c)::value;
     constexpr int RB = 64 * E;                       // bytes per staged row
     constexpr int CPR = RB / 16;                     // 16-byte chunks per row
     constexpr int RP = kEpiWaveBytes / RB;           // rows per pass: 128 (bf16) or 64 (fp32)
@@ -771,11 +897,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c0 = 32 * fj + 8 * q + 4 * lg;   // first of this lane's 4 columns
-          float bv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (BIAS) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) bv[e] = bias[wcol0 + c0 + e];
-          }
 #pragma unroll
           for (int fl = 0; fl < FPP; ++fl) {
             const int fi = pass * FPP + fl;
@@ -783,17 +904,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
             const uint32_t byte = (uint32_t)(c0 * E);
             const uint32_t chunk = (byte >> 4) ^ (uint32_t)(row & (CPR - 1) & 7);
             const uint32_t addr = wbase + (uint32_t)row * RB + (chunk << 4) + (byte & 15);
-            if (Y_BF16) {
+            if (E == 2) {
               typedef uint32_t v2u __attribute__((ext_vector_type(2)));
               v2u p;
-              p[0] = pack_bf16(value(fi, fj, 4 * q + 0, bv[0]), value(fi, fj, 4 * q + 1, bv[1]));
-              p[1] = pack_bf16(value(fi, fj, 4 * q + 2, bv[2]), value(fi, fj, 4 * q + 3, bv[3]));
+              p[0] = pack_bf16(acc[fi][fj][4 * q + 0], acc[fi][fj][4 * q + 1]);
+              p[1] = pack_bf16(acc[fi][fj][4 * q + 2], acc[fi][fj][4 * q + 3]);
               *reinterpret_cast<v2u*>(smem + addr) = p;
             } else {
               typedef float v4f __attribute__((ext_vector_type(4)));
               v4f p;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) p[e] = value(fi, fj, 4 * q + e, bv[e]);
+              for (int e = 0; e < 4; ++e) p[e] = acc[fi][fj][4 * q + e];
               *reinterpret_cast<v4f*>(smem + addr) = p;
             }
           }
@@ -806,11 +927,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
         const int c = lane % CPR;
         const uint32_t addr = wbase + (uint32_t)row * RB + (uint32_t)((c ^ (row & (CPR - 1) & 7)) << 4);
         const v4i v = *reinterpret_cast<const v4i*>(smem + addr);
-        uint8_t* dst = reinterpret_cast<uint8_t*>(y) +
-                       ((int64_t)(wrow0 + pass * RP + row) * ld_y + wcol0) * E + 16 * c;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(ep.y) +
+                       ((int64_t)(wrow0 + pass * RP + row) * ep.ld_y + wcol0) * E + 16 * c;
         *reinterpret_cast<v4i*>(dst) = v;
       }
     }
+  };
+  if (!ep.y) {
+  } else if (ep.y_vec16 && m0 + BM <= M && n0 + BN <= N) {
+    if (ep.y_bf16)
+      store_staged(std::integral_constant<int, 2>());
+    else
+      store_staged(std::integral_constant<int, 4>());
   } else {
 #pragma unroll
     for (int fj = 0; fj < 2; ++fj)
@@ -819,28 +947,59 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int col = wcol0 + 32 * fj + 8 * q + 4 * lg + e;
-          const float bv = (BIAS && col < N) ? bias[col] : 0.0f;
 #pragma unroll
           for (int fi = 0; fi < 4; ++fi) {
             const int row = wrow0 + 32 * fi + li;
             if (row < M && col < N) {
-              const float v = value(fi, fj, 4 * q + e, bv);
-              if (Y_BF16)
-                reinterpret_cast<uint16_t*>(y)[(int64_t)row * ld_y + col] = (uint16_t)f32_to_bf16_rne(v);
+              const float v = acc[fi][fj][4 * q + e];
+              if (ep.y_bf16)
+                reinterpret_cast<uint16_t*>(ep.y)[(int64_t)row * ep.ld_y + col] = (uint16_t)f32_to_bf16_rne(v);
               else
-                reinterpret_cast<float*>(y)[(int64_t)row * ld_y + col] = v;
+                reinterpret_cast<float*>(ep.y)[(int64_t)row * ep.ld_y + col] = v;
             }
           }
         }
   }
+  if (ep.qc) {
+    // bf16(v) of the wave's 128x64 block as 128 rows of 128 bytes in its own LDS region
+    // (the same region and chunk swizzle as the bf16 staging above), columns >= N as +0
+    const uint32_t wbase = (uint32_t)wid * kEpiWaveBytes;
+#pragma unroll
+    for (int fj = 0; fj < 2; ++fj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c0 = 32 * fj + 8 * q + 4 * lg;
+        bool in[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) in[e] = wcol0 + c0 + e < N;
+#pragma unroll
+        for (int fi = 0; fi < 4; ++fi) {
+          const int row = 32 * fi + li;
+          const uint32_t chunk = (uint32_t)(((2 * c0) >> 4) ^ (row & 7));
+          const uint32_t addr = wbase + (uint32_t)row * 128u + (chunk << 4) + (uint32_t)((2 * c0) & 15);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = in[e] ? acc[fi][fj][4 * q + e] : 0.0f;
+          typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+          v2u p;
+          p[0] = pack_bf16(v[0], v[1]);
+          p[1] = pack_bf16(v[2], v[3]);
+          *reinterpret_cast<v2u*>(smem + addr) = p;
+        }
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    quantize_staged<2>(wbase, lane, wrow0, M, wcol0 / 32, (N + 31) / 32, ep);
+  }
 }
 
-template <int FA, int FB, int Y_BF16, bool BIAS>
-hipError_t launch_t(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
-                    int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, float alpha,
-                    const float* bias, void* y, int64_t ld_y, hipStream_t stream) {
+template <int FA, int FB>
+hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
+                    int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
+                    const GemmEpilogue& ep, hipStream_t stream) {
   static bool attr_set[64] = {false};
-  auto kern = k_gemm_pp<FA, FB, Y_BF16, BIAS>;
+  auto kern = k_gemm_pp<FA, FB>;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (!attr_set[dev]) {
@@ -849,45 +1008,28 @@ hipError_t launch_t(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t 
     attr_set[dev] = true;
   }
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  const int E = Y_BF16 ? 2 : 4;
-  const int y_vec16 = ((uintptr_t)y % 16 == 0) && ((ld_y * E) % 16 == 0);
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreads), kLdsBytes, stream, (int)M, (int)N, (int)K, tiles_m,
-                     tiles_n, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, y_vec16);
+                     tiles_n, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep);
   return hipGetLastError();
 }
 
-template <int FA, int FB>
-hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
-                    int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, float alpha,
-                    const float* bias, void* y, int y_bf16, int64_t ld_y, hipStream_t stream) {
-  if (y_bf16) {
-    if (bias) return launch_t<FA, FB, 1, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
-    return launch_t<FA, FB, 1, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
-  }
-  if (bias) return launch_t<FA, FB, 0, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
-  return launch_t<FA, FB, 0, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
-}
-
 hipError_t launch(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
-                  int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, int w_fmt, float alpha,
-                  const float* bias, void* y, int y_bf16, int64_t ld_y, hipStream_t stream) {
-  if (x_fmt == kE4M3 && w_fmt == kE4M3)
-    return launch_f<0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
-  if (x_fmt == kE4M3)
-    return launch_f<0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
-  if (w_fmt == kE4M3)
-    return launch_f<1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
-  return launch_f<1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
+                  int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, int w_fmt,
+                  const GemmEpilogue& ep, hipStream_t stream) {
+  if (x_fmt == kE4M3 && w_fmt == kE4M3) return launch_f<0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+  if (x_fmt == kE4M3) return launch_f<0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+  if (w_fmt == kE4M3) return launch_f<1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+  return launch_f<1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
 }
 
 }  // namespace pp
 
-template <int MODE, int FA, int FB, int Y_BF16, bool BIAS>
-hipError_t gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
-                  const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, float alpha, const float* bias,
-                  void* y, int64_t ld_y, hipStream_t stream) {
+template <int MODE, int FA, int FB>
+hipError_t gemm_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
+                  const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, const GemmEpilogue& ep,
+                  hipStream_t stream) {
   static bool attr_set[64] = {false};
-  auto kern = k_gemm<MODE, FA, FB, Y_BF16, BIAS>;
+  auto kern = k_gemm<MODE, FA, FB>;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (!attr_set[dev]) {
@@ -898,48 +1040,32 @@ hipError_t gemm_t(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
   hipLaunchKernelGGL(kern, dim3(ntiles), dim3(kThreads), kLdsBytes, stream, (int)M, (int)N, (int)K, tiles_m, tiles_n,
-                     xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y);
+                     xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep);
   return hipGetLastError();
-}
-
-template <int MODE, int FA, int FB>
-hipError_t gemm_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
-                  const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, float alpha, const float* bias,
-                  void* y, int y_bf16, int64_t ld_y, hipStream_t stream) {
-  if (y_bf16) {
-    if (bias) return gemm_t<MODE, FA, FB, 1, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
-    return gemm_t<MODE, FA, FB, 1, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
-  }
-  if (bias) return gemm_t<MODE, FA, FB, 0, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
-  return gemm_t<MODE, FA, FB, 0, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, ld_y, stream);
 }
 
 template <int MODE>
 hipError_t gemm_m(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
-                  int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, int w_fmt, float alpha,
-                  const float* bias, void* y, int y_bf16, int64_t ld_y, hipStream_t stream) {
-  if (x_fmt == kE4M3 && w_fmt == kE4M3)
-    return gemm_f<MODE, 0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
-  if (x_fmt == kE4M3)
-    return gemm_f<MODE, 0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
-  if (w_fmt == kE4M3)
-    return gemm_f<MODE, 1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
-  return gemm_f<MODE, 1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, alpha, bias, y, y_bf16, ld_y, stream);
+                  int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, int w_fmt,
+                  const GemmEpilogue& ep, hipStream_t stream) {
+  if (x_fmt == kE4M3 && w_fmt == kE4M3) return gemm_f<MODE, 0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+  if (x_fmt == kE4M3) return gemm_f<MODE, 0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+  if (w_fmt == kE4M3) return gemm_f<MODE, 1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+  return gemm_f<MODE, 1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
                        int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
-                       int w_fmt, float alpha, const float* bias, void* y, int y_bf16, int64_t ld_y, int exact,
-                       hipStream_t stream) {
+                       int w_fmt, const GemmEpilogue& ep_in, int exact, hipStream_t stream) {
+  GemmEpilogue ep = ep_in;
+  const int64_t ey = ep.y_bf16 ? 2 : 4;
+  ep.y_vec16 = ep.y && ((uintptr_t)ep.y % 16 == 0) && ((ep.ld_y * ey) % 16 == 0);
   const bool scales16 = ((uintptr_t)xs % 16 == 0) && ((uintptr_t)ws % 16 == 0) && ld_xs % 16 == 0 && ld_ws % 16 == 0;
-  if (!exact && scales16)
-    return pp::launch(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, alpha, bias, y, y_bf16, ld_y,
-                      stream);
-  if (exact)
-    return gemm_m<1>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, alpha, bias, y, y_bf16, ld_y, stream);
-  return gemm_m<0>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, alpha, bias, y, y_bf16, ld_y, stream);
+  if (!exact && scales16) return pp::launch(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, ep, stream);
+  if (exact) return gemm_m<1>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, ep, stream);
+  return gemm_m<0>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, ep, stream);
 }
 
 }  // namespace mxq

@@ -31,10 +31,29 @@ hipError_t launch_dequant(const uint8_t* codes, int64_t ld_codes, const uint8_t*
                           int fmt, int64_t L, int64_t K, void* dst, int dst_bf16, int64_t ld_dst,
                           bool vec, hipStream_t stream);
 
+// What a GEMM launch writes: v = act(alpha * acc + bias[col]) (act 0: identity, 1: SiLU);
+// y (may be null) receives v rounded to its type; qc/qs (qc may be null) receive the MX
+// codes (format q_fmt) and E8M0 scales of bf16(v) in 32-column blocks along N, i.e. the
+// bytes the rowwise quantize gives for a bf16 Y.  y_vec16: y and its rows are 16-byte
+// aligned.
+struct GemmEpilogue {
+  float alpha;
+  const float* bias;
+  int act;
+  void* y;
+  int y_bf16;
+  int64_t ld_y;
+  int y_vec16;
+  uint8_t* qc;
+  int64_t ld_qc;
+  uint8_t* qs;
+  int64_t ld_qs;
+  int q_fmt;
+};
+
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K,
                        const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_fmt,
                        const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws, int w_fmt,
-                       float alpha, const float* bias, void* y, int y_bf16, int64_t ld_y, int exact,
-                       hipStream_t stream);
+                       const GemmEpilogue& ep, int exact, hipStream_t stream);
 
 }  // namespace mxq

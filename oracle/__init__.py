@@ -49,6 +49,10 @@ def lib():
         u8p = ctypes.POINTER(ctypes.c_uint8)
         i64 = ctypes.c_int64
         vp = ctypes.c_void_p
+        L.mxo_silu.restype = ctypes.c_double
+        L.mxo_silu.argtypes = [ctypes.c_double]
+        L.mxo_silu_array.restype = None
+        L.mxo_silu_array.argtypes = [vp, vp, i64]
         L.mxo_decode.restype = ctypes.c_double
         L.mxo_decode.argtypes = [ctypes.c_uint8, ctypes.c_int]
         L.mxo_decode_e8m0.restype = ctypes.c_double
@@ -162,6 +166,17 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str, K: int, out: str
         lib().mxo_dequantize(_ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1], FMT[fmt],
                              L, K, _ptr(dst), SRC[out], K)
     return dst
+
+
+def silu(v):
+    """SiLU in FP64 of a scalar or an array (values converted to FP64 first)."""
+    if np.isscalar(v):
+        return lib().mxo_silu(float(v))
+    a = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty_like(a)
+    if a.size:
+        lib().mxo_silu_array(_ptr(a), _ptr(out), a.size)
+    return out
 
 
 def gemm(x_codes, x_scales, x_fmt, w_codes, w_scales, w_fmt, K, alpha=1.0, bias=None):

@@ -29,6 +29,7 @@
  *   - A block containing NaN or +-Inf gets scale byte 255 and every code 0x7F.
  *   - Padding positions (k >= K inside the last block) get code 0x00.
  *   - The GEMM epilogue is y = alpha*acc + bias[j] (scale, then bias), done in FP64 here.
+ *   - The epilogue activation (SiLU) is applied after the scale and the bias.
  */
 #include <math.h>
 #include <stdint.h>
@@ -349,4 +350,17 @@ void mxo_gemm_sampled(int64_t K,
     for (int64_t s = 0; s < n; ++s)
         gemm_one(ii[s], jj[s], K, x_codes, ld_x, x_scales, ld_xs, x_fmt, w_codes, ld_w, w_scales,
                  ld_ws, w_fmt, alpha, bias, &y_ref[s], &t[s]);
+}
+
+/* ---------------------------------------------------------------- activation ------ */
+
+/* SiLU, the activation the kernel contract's epilogue names [LPGP "Hardware support and
+ * kernel ABI contracts"], by its textbook definition v * sigmoid(v) = v / (1 + e^-v) in
+ * FP64 (exact for every purpose here: FP64 keeps ~1e-16 relative error while every
+ * comparison is against FP32 or narrower).                                              */
+double mxo_silu(double v) { return v / (1.0 + exp(-v)); }
+
+void mxo_silu_array(const double *v, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = mxo_silu(v[i]);
 }

@@ -18,8 +18,8 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert {"mxq_quantize", "mxq_quantize_dual", "mxq_dequantize", "mxq_gemm", "mxq_status_string",
-            "mxq_version"} <= set(declared_symbols())
+    assert {"mxq_quantize", "mxq_quantize_dual", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex",
+            "mxq_status_string", "mxq_version"} <= set(declared_symbols())
 
 
 def test_library_exports_every_declared_symbol():
@@ -131,6 +131,35 @@ def test_gemm_validation():
     assert g(bias=FAKE + 2) == -4
     assert g(M=0, xc=None, y=None) == 0
     assert g(N=0, wc=None, y=None) == 0
+
+
+def gx(**kw):
+    a = dict(M=8, N=40, K=64, xc=FAKE, ld_x=64, xs=FAKE, ld_xs=2, xe=mxq.MXQ_E4M3, wc=FAKE, ld_w=64, ws=FAKE,
+             ld_ws=2, we=mxq.MXQ_E4M3, alpha=1.0, bias=None, act=mxq.MXQ_ACT_SILU, y=None, yt=mxq.MXQ_BF16, ld_y=0,
+             qe=mxq.MXQ_E4M3, qc=FAKE, ld_qc=64, qs=FAKE, ld_qs=2, acc=0)     # N = 40 -> Np = 64
+    a.update(kw)
+    return mxq.mxq_gemm_ex(a["M"], a["N"], a["K"], a["xc"], a["ld_x"], a["xs"], a["ld_xs"], a["xe"], a["wc"],
+                           a["ld_w"], a["ws"], a["ld_ws"], a["we"], a["alpha"], a["bias"], a["act"], a["y"],
+                           a["yt"], a["ld_y"], a["qe"], a["qc"], a["ld_qc"], a["qs"], a["ld_qs"], a["acc"], None)
+
+
+def test_gemm_ex_validation():
+    assert gx(act=2) == -6
+    assert gx(act=-1) == -6
+    assert gx(qe=mxq.MXQ_BF16) == -5
+    assert gx(y=FAKE, yt=mxq.MXQ_E4M3, ld_y=40) == -5
+    assert gx(qc=None) == -1                  # neither output
+    assert gx(qs=None) == -1
+    assert gx(ld_qc=48) == -3                 # < Np = 64
+    assert gx(ld_qs=1) == -3
+    assert gx(ld_qc=72) == -4                 # not a multiple of 16
+    assert gx(qc=FAKE + 8) == -4
+    assert gx(y=FAKE, ld_y=39) == -3
+    assert gx(y=FAKE + 1, ld_y=40) == -4
+    assert gx(alpha=float("nan")) == -6
+    assert gx(M=0, xc=None, qc=None, qs=None) == 0
+    # mxq_gemm keeps requiring y
+    assert g(y=None) == -1
 
 
 def test_dequantize_validation():
