@@ -229,6 +229,41 @@ def main():
     xq_ms = xa.elapsed_time(xb) / 20
     xq_gbs = M * K * (2 + 1 + 1 / 32) / (xq_ms * 1e-3) / 1e9
 
+    # ---- FFN up projection with bias and SiLU (T=16384, H=5120, I=8192).  Unfused: the GEMM
+    #      writes bf16 Y1, then the rowwise quantize of Y1 that the down projection consumes.
+    #      Fused: the GEMM epilogue writes Y1's MX codes and scales directly (same bytes).
+    d3 = wl.workload3()
+    T3, H3, I3 = d3["T"], d3["H"], d3["I"]
+    f_xc, f_xs = mxq.quantize(d3["x"].to(dev), "e4m3", "row")
+    f_wc, f_ws = mxq.quantize(d3["w1"].to(dev), "e4m3", "row")
+    f_b = d3["b1"].to(dev)
+    del d3
+    y1 = torch.empty((T3, I3), dtype=torch.bfloat16, device=dev)
+    y1c = torch.empty((T3, I3), dtype=torch.uint8, device=dev)
+    y1s = torch.empty((T3, I3 // 32), dtype=torch.uint8, device=dev)
+
+    def up_args(yp, yld, qc, qld, qs, qsld):
+        return (T3, I3, H3, f_xc.data_ptr(), f_xc.stride(0), f_xs.data_ptr(), f_xs.stride(0), mxq.MXQ_E4M3,
+                f_wc.data_ptr(), f_wc.stride(0), f_ws.data_ptr(), f_ws.stride(0), mxq.MXQ_E4M3, ctypes.c_float(1.0),
+                f_b.data_ptr(), mxq.MXQ_ACT_SILU, yp, mxq.MXQ_BF16, yld, mxq.MXQ_E4M3, qc, qld, qs, qsld,
+                mxq.MXQ_ACC_FP8_MFMA, sh)
+    up_unfused = up_args(y1.data_ptr(), y1.stride(0), None, 0, None, 0)
+    q_y1 = (y1.data_ptr(), mxq.MXQ_BF16, T3, I3, y1.stride(0), mxq.MXQ_ROWWISE, mxq.MXQ_E4M3, y1c.data_ptr(),
+            y1c.stride(0), y1s.data_ptr(), y1s.stride(0), sh)
+    up_fused = up_args(None, 0, y1c.data_ptr(), y1c.stride(0), y1s.data_ptr(), y1s.stride(0))
+    for a in (L.mxq_gemm_ex(*up_unfused), L.mxq_quantize(*q_y1), L.mxq_gemm_ex(*up_fused)):
+        if a != 0:
+            raise RuntimeError("mxq call failed: %s" % mxq.mxq_status_string(a))
+
+    def unfused_pair():
+        L.mxq_gemm_ex(*up_unfused)
+        L.mxq_quantize(*q_y1)
+    up_gemm_ms = time_calls(lambda: L.mxq_gemm_ex(*up_unfused))
+    up_unfused_ms = time_calls(unfused_pair)
+    up_fused_ms = time_calls(lambda: L.mxq_gemm_ex(*up_fused))
+    up_flops = 2.0 * T3 * I3 * H3
+    del f_xc, f_xs, f_wc, f_ws, f_b, y1, y1c, y1s
+
     traffic = load_traffic("gemm")
     out = {
         "metric": "MXFP8 GEMM TFLOP/s (% dense MFMA peak); mx_quantize GB/s (% HBM peak)",
@@ -260,6 +295,13 @@ def main():
             "quantize_2p28_dual": {"ms": round(dual_ms, 5), "gbs": round(dual_bytes / (dual_ms * 1e-3) / 1e9, 1),
                                    "vs_two_calls_ms": round(q_ms + col_ms, 5)},
             "dequantize_2p28_bf16": {"ms": round(dq_ms, 5), "gbs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1)},
+            "ffn_up_silu_unfused": {"ms": round(up_unfused_ms, 5), "gemm_ms": round(up_gemm_ms, 5),
+                                    "gemm_tflops": round(up_flops / (up_gemm_ms * 1e-3) / 1e12, 2),
+                                    "what": "T=16384 H=5120 I=8192 GEMM (bias, SiLU, bf16 Y1) + quantize(Y1)"},
+            "ffn_up_silu_fused": {"ms": round(up_fused_ms, 5),
+                                  "tflops": round(up_flops / (up_fused_ms * 1e-3) / 1e12, 2),
+                                  "speedup_vs_unfused": round(up_unfused_ms / up_fused_ms, 3),
+                                  "what": "same GEMM writing Y1's MX codes and scales from its epilogue"},
             "quantize_2p28": {"ms": round(q_ms, 5), "gbs": round(q_gbs, 1), "frac_hbm": round(q_gbs / PEAK_HBM_GBS, 4),
                               "bytes": int(q_bytes), "workload": "[16384][16384] bf16 Laplace(0,1) 1% x1e4, rowwise E4M3"},
         },
