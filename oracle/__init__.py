@@ -49,6 +49,13 @@ def lib():
         u8p = ctypes.POINTER(ctypes.c_uint8)
         i64 = ctypes.c_int64
         vp = ctypes.c_void_p
+        L.mxo_encode_sr.restype = ctypes.c_uint8
+        L.mxo_encode_sr.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_uint32]
+        L.mxo_philox4x32_10.restype = None
+        L.mxo_philox4x32_10.argtypes = [vp, vp, vp]
+        L.mxo_quantize_sr.restype = None
+        L.mxo_quantize_sr.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
+                                      vp, i64, vp, i64]
         L.mxo_silu.restype = ctypes.c_double
         L.mxo_silu.argtypes = [ctypes.c_double]
         L.mxo_silu_array.restype = None
@@ -153,6 +160,35 @@ def quantize(src: np.ndarray, fmt: str, axis: int = 0):
     if L > 0 and K > 0:
         lib().mxo_quantize(_ptr(src), _src_type(src), rows, cols, cols, axis, FMT[fmt],
                            _ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1])
+    return codes[:, :Kp], scales[:, :Kp // 32]
+
+
+def encode_sr(a: float, fmt: str, r24: int) -> int:
+    """Stochastically rounded code of the exact value a under the 24-bit random integer r24."""
+    return int(lib().mxo_encode_sr(float(a), FMT[fmt], int(r24)))
+
+
+def philox4x32_10(counter, key):
+    """Philox4x32-10 block: four 32-bit counter words, two key words -> four output words."""
+    c = np.ascontiguousarray(counter, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().mxo_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return [int(v) for v in out]
+
+
+def quantize_sr(src: np.ndarray, fmt: str, seed: int, axis: int = 0):
+    """quantize() with stochastically rounded codes; element n = line * Kp + k draws word
+    n % 4 of Philox4x32-10(counter (n // 4), key = seed) and keeps its top 24 bits."""
+    src = np.ascontiguousarray(src)
+    rows, cols = src.shape
+    L, K = (rows, cols) if axis == 0 else (cols, rows)
+    Kp = 32 * ((K + 31) // 32)
+    codes = np.zeros((L, max(Kp, 1)), dtype=np.uint8)
+    scales = np.zeros((L, max(Kp // 32, 1)), dtype=np.uint8)
+    if L > 0 and K > 0:
+        lib().mxo_quantize_sr(_ptr(src), _src_type(src), rows, cols, cols, axis, FMT[fmt], int(seed) & (2 ** 64 - 1),
+                              _ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1])
     return codes[:, :Kp], scales[:, :Kp // 32]
 
 

@@ -30,6 +30,10 @@
  *   - Padding positions (k >= K inside the last block) get code 0x00.
  *   - The GEMM epilogue is y = alpha*acc + bias[j] (scale, then bias), done in FP64 here.
  *   - The epilogue activation (SiLU) is applied after the scale and the bias.
+ *   - Stochastic rounding: element n (its index line*Kp + k in the padded code array) draws
+ *     the 32-bit word n%4 of Philox4x32-10(counter = (n/4 low, n/4 high, 0, 0), key = seed);
+ *     its top 24 bits r decide: round up iff r < 2^24 * (|a| - l) / (u - l).  The scale
+ *     rule is unchanged.
  */
 #include <math.h>
 #include <stdint.h>
@@ -150,6 +154,66 @@ uint8_t mxo_encode(double a, int fmt)
     return (uint8_t)(sign | code);
 }
 
+/* Stochastic rounding of an exact real value a to an FP8 code [LPGP "Rounding: RNE
+ * versus stochastic rounding"]: with l <= |a| < u the neighbouring finite magnitudes, the
+ * result is u with probability (|a| - l) / (u - l), else l; a representable |a| stays.
+ * The probability is realised by a uniform 24-bit integer r: up iff r < 2^24 * p.  (p is
+ * a dyadic rational here and 2^24 * p is computed exactly in FP64.)  |a| >= fmax gives
+ * fmax; sign as in mxo_encode; NaN gives 0x7F.                                           */
+uint8_t mxo_encode_sr(double a, int fmt, uint32_t r24)
+{
+    build_tables();
+    if (isnan(a)) return 0x7F;
+    uint8_t sign = signbit(a) ? 0x80 : 0x00;
+    double x = fabs(a);
+    int n = g_nmag[fmt];
+    const double *t = g_mag[fmt];
+    if (x >= t[n - 1]) return (uint8_t)(sign | (n - 1));
+    int lo = 0, hi = n - 1;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (t[mid] <= x) lo = mid; else hi = mid;
+    }
+    if (x == t[lo]) return (uint8_t)(sign | lo);
+    double p = (x - t[lo]) / (t[hi] - t[lo]);
+    int code = (double)r24 < p * 16777216.0 ? hi : lo;
+    return (uint8_t)(sign | code);
+}
+
+/* ---------------------------------------------------------------- random numbers -- */
+
+/* Philox4x32-10 [Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2,
+ * 3", SC 2011]: ten rounds of two 32x32->64-bit multiplications (multipliers 0xD2511F53,
+ * 0xCD9E8D57) whose high halves are xored with the other counter words and the key; the
+ * key is bumped by the Weyl constants 0x9E3779B9, 0xBB67AE85 between rounds.             */
+void mxo_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; ++r) {
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        uint32_t n1 = (uint32_t)p1;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        uint32_t n3 = (uint32_t)p0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The 24-bit uniform integer of element n under a 64-bit seed. */
+static uint32_t sr_random24(uint64_t seed, uint64_t n)
+{
+    uint32_t ctr[4] = {(uint32_t)(n >> 2), (uint32_t)(n >> 34), 0u, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    mxo_philox4x32_10(ctr, key, out);
+    return out[n & 3] >> 8;
+}
+
 /* ---------------------------------------------------------------- scale rule ------ */
 
 /* Conservative power-of-two block scale [LPGP "Microscaling: the two-row experiment";
@@ -224,7 +288,7 @@ static float to_f32(double v)
  * blocks [LPGP "Scale ownership and the GEMM dataflow": block index b along K; partial
  * final block zero-padded].                                                              */
 static void quantize_line(const void *src, int src_type, int64_t base, int64_t stride, int64_t K,
-                          int fmt, uint8_t *codes, uint8_t *scales)
+                          int fmt, uint8_t *codes, uint8_t *scales, int sr, uint64_t seed, int64_t n0)
 {
     int64_t nb = (K + 31) / 32;
     for (int64_t b = 0; b < nb; ++b) {
@@ -247,7 +311,9 @@ static void quantize_line(const void *src, int src_type, int64_t base, int64_t s
         for (int64_t k = k0; k < k0 + 32; ++k) {
             if (k < K) {
                 double x = load_elem(src, src_type, base + k * stride);
-                codes[k] = mxo_encode(ldexp(x, -e), fmt);  /* x / S, exact in FP64 */
+                double a = ldexp(x, -e);                   /* x / S, exact in FP64 */
+                codes[k] = sr ? mxo_encode_sr(a, fmt, sr_random24(seed, (uint64_t)(n0 + k)))
+                              : mxo_encode(a, fmt);
             } else {
                 codes[k] = 0x00;                            /* zero padding */
             }
@@ -259,20 +325,37 @@ static void quantize_line(const void *src, int src_type, int64_t base, int64_t s
  * axis 1 (colwise): the lines are the columns of src, K = rows, and the output is stored
  *                   transposed, codes [cols][ld_codes], scales [cols][ld_scales].
  * Writes Kp = 32*ceil(K/32) codes and Kp/32 scale bytes per line.                        */
-void mxo_quantize(const void *src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
-                  int axis, int fmt, uint8_t *codes, int64_t ld_codes, uint8_t *scales,
-                  int64_t ld_scales)
+static void quantize_any(const void *src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
+                         int axis, int fmt, uint8_t *codes, int64_t ld_codes, uint8_t *scales,
+                         int64_t ld_scales, int sr, uint64_t seed)
 {
     build_tables();
     int64_t L = axis == 0 ? rows : cols;
     int64_t K = axis == 0 ? cols : rows;
+    int64_t Kp = 32 * ((K + 31) / 32);
     #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t l = 0; l < L; ++l) {
         int64_t base = axis == 0 ? l * ld_src : l;
         int64_t stride = axis == 0 ? 1 : ld_src;
         quantize_line(src, src_type, base, stride, K, fmt, codes + l * ld_codes,
-                      scales + l * ld_scales);
+                      scales + l * ld_scales, sr, seed, l * Kp);
     }
+}
+
+void mxo_quantize(const void *src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
+                  int axis, int fmt, uint8_t *codes, int64_t ld_codes, uint8_t *scales,
+                  int64_t ld_scales)
+{
+    quantize_any(src, src_type, rows, cols, ld_src, axis, fmt, codes, ld_codes, scales, ld_scales, 0, 0);
+}
+
+/* The same blocks and scales with stochastically rounded codes (the readings above give
+ * the random-number contract).                                                          */
+void mxo_quantize_sr(const void *src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
+                     int axis, int fmt, uint64_t seed, uint8_t *codes, int64_t ld_codes,
+                     uint8_t *scales, int64_t ld_scales)
+{
+    quantize_any(src, src_type, rows, cols, ld_src, axis, fmt, codes, ld_codes, scales, ld_scales, 1, seed);
 }
 
 /* ---------------------------------------------------------------- dequantize ------ */
