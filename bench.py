@@ -200,6 +200,12 @@ def main():
     q_col = list(q_q)
     q_col[5] = mxq.MXQ_COLWISE
     col_ms = time_calls(lambda: L.mxq_quantize(*q_col))
+    # stochastically rounded E5M2 (gradients): same bytes, Philox random numbers per element
+    q_sr = (qx.data_ptr(), mxq.MXQ_BF16, qx.shape[0], qx.shape[1], qx.stride(0), mxq.MXQ_ROWWISE, mxq.MXQ_E5M2,
+            ctypes.c_uint64(20261202), qc.data_ptr(), qc.stride(0), qs.data_ptr(), qs.stride(0), sh)
+    if L.mxq_quantize_sr(*q_sr) != 0:
+        raise RuntimeError("mxq_quantize_sr failed")
+    sr_ms = time_calls(lambda: L.mxq_quantize_sr(*q_sr))
     # both orientations from one read of the tensor (rowwise into qc/qs, columnwise into
     # separate [cols][rows] outputs): 2 B read + 2 x (1 + 1/32) B written per element
     dc = torch.empty((qx.shape[1], qx.shape[0]), dtype=torch.uint8, device=dev)
@@ -292,6 +298,8 @@ def main():
             "quantize_x": {"ms": round(xq_ms, 5), "gbs": round(xq_gbs, 1), "bytes": int(M * K * 3.03125)},
             "quantize_2p28_e5m2": {"ms": round(e5_ms, 5), "gbs": round(q_bytes / (e5_ms * 1e-3) / 1e9, 1)},
             "quantize_2p28_colwise": {"ms": round(col_ms, 5), "gbs": round(q_bytes / (col_ms * 1e-3) / 1e9, 1)},
+            "quantize_2p28_sr_e5m2": {"ms": round(sr_ms, 5), "gbs": round(q_bytes / (sr_ms * 1e-3) / 1e9, 1),
+                                      "rounding": "stochastic (Philox4x32-10)"},
             "quantize_2p28_dual": {"ms": round(dual_ms, 5), "gbs": round(dual_bytes / (dual_ms * 1e-3) / 1e9, 1),
                                    "vs_two_calls_ms": round(q_ms + col_ms, 5)},
             "dequantize_2p28_bf16": {"ms": round(dq_ms, 5), "gbs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1)},

@@ -118,6 +118,26 @@ int mxq_quantize(const void* src, int src_type, int64_t rows, int64_t cols, int6
                  int64_t ld_scales, void* stream);
 
 /*
+ * mxq_quantize_sr -- mxq_quantize with stochastically rounded codes (gradients).
+ * ("Rounding: RNE versus stochastic rounding": between the neighbouring representable
+ * values l <= x < u, round up with probability (x - l) / (u - l), so E[SR(x)] = x and
+ * representable values stay; applied to gradients, not every tensor.)
+ *
+ * Arguments, layouts, validation and scale bytes exactly as mxq_quantize (the scale rule
+ * is unchanged, so x / S never exceeds fmax and nothing is clipped); only the codes
+ * differ.  Random numbers: the element at index n = line * Kp + k of the padded code
+ * array (line = row for MXQ_ROWWISE, column for MXQ_COLWISE) draws word n % 4 of
+ * Philox4x32-10 (Salmon et al., SC 2011) with counter (n / 4 mod 2^32, n / 4 >> 32, 0, 0)
+ * and key (seed mod 2^32, seed >> 32), and keeps its top 24 bits r; the code rounds up
+ * iff r < 2^24 * (|x/S| - l) / (u - l), decided exactly.  Same seed and shape -> the same
+ * bytes, independent of the launch configuration.  Pad codes are 0x00; a NaN/Inf block
+ * is 0x7F throughout, as for mxq_quantize.
+ */
+int mxq_quantize_sr(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
+                    int axis, int elem, uint64_t seed, uint8_t* codes, int64_t ld_codes,
+                    uint8_t* scales, int64_t ld_scales, void* stream);
+
+/*
  * mxq_quantize_dual -- both orientations of one matrix from a single read of it.
  * ("Microscaling: the two-row experiment", closing paragraph: moving from 1x32 to 32x1
  * groups changes which values share a scale, so the second orientation is derived from

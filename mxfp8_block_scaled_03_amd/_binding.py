@@ -44,6 +44,8 @@ def lib():
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.mxq_quantize.restype = ci
         L.mxq_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, vp, i64, vp, i64, vp]
+        L.mxq_quantize_sr.restype = ci
+        L.mxq_quantize_sr.argtypes = [vp, ci, i64, i64, i64, ci, ci, ctypes.c_uint64, vp, i64, vp, i64, vp]
         L.mxq_quantize_dual.restype = ci
         L.mxq_quantize_dual.argtypes = [vp, ci, i64, i64, i64, ci, vp, i64, vp, i64, vp, i64, vp, i64, vp]
         L.mxq_dequantize.restype = ci
@@ -68,6 +70,12 @@ def mxq_quantize(src, src_type, rows, cols, ld_src, axis, elem, codes, ld_codes,
                  stream=None) -> int:
     return lib().mxq_quantize(src, src_type, rows, cols, ld_src, axis, elem, codes, ld_codes, scales,
                               ld_scales, stream)
+
+
+def mxq_quantize_sr(src, src_type, rows, cols, ld_src, axis, elem, seed, codes, ld_codes, scales, ld_scales,
+                    stream=None) -> int:
+    return lib().mxq_quantize_sr(src, src_type, rows, cols, ld_src, axis, elem, seed, codes, ld_codes, scales,
+                                 ld_scales, stream)
 
 
 def mxq_quantize_dual(src, src_type, rows, cols, ld_src, elem, row_codes, ld_row_codes, row_scales, ld_row_scales,
@@ -161,6 +169,26 @@ def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None):
                       _ELEM[elem], codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0),
                       _stream_handle())
     _check(st, "mxq_quantize")
+    return codes, scales
+
+
+def quantize_sr(x, seed: int, elem: str = "e5m2", axis: str = "row", codes=None, scales=None):
+    """quantize() with stochastically rounded codes (Philox4x32-10 keyed by `seed`, see
+    mxq_quantize_sr); E5M2 by default, the gradient format."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("quantize_sr expects a 2-D tensor with unit stride along the last dimension")
+    rows, cols = x.shape
+    L, K = (rows, cols) if axis == "row" else (cols, rows)
+    Kp = _round_up(K, 32)
+    if codes is None:
+        codes = torch.empty((L, Kp), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((L, _round_up(Kp // 32, 16)), dtype=torch.uint8, device=x.device)[:, :Kp // 32]
+    st = mxq_quantize_sr(x.data_ptr(), _wide_type(x), rows, cols, x.stride(0) if rows > 0 else cols,
+                         MXQ_ROWWISE if axis == "row" else MXQ_COLWISE, _ELEM[elem], int(seed) & (2 ** 64 - 1),
+                         codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0), _stream_handle())
+    _check(st, "mxq_quantize_sr")
     return codes, scales
 
 

@@ -27,6 +27,13 @@ hipError_t launch_quant_dual(const void* src, int src_bf16, int64_t rows, int64_
                              uint8_t* rcodes, int64_t ld_rc, uint8_t* rscales, int64_t ld_rs, uint8_t* ccodes,
                              int64_t ld_cc, uint8_t* cscales, int64_t ld_cs, bool vec, hipStream_t stream);
 
+// Quantize with stochastically rounded codes (rowwise, or colwise with transposed output);
+// seed keys the Philox4x32-10 stream, element n of the padded code array draws word n % 4
+// of counter n / 4.
+hipError_t launch_quant_sr(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, bool colwise,
+                           int fmt, uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec,
+                           uint64_t seed, hipStream_t stream);
+
 hipError_t launch_dequant(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales, int64_t ld_scales,
                           int fmt, int64_t L, int64_t K, void* dst, int dst_bf16, int64_t ld_dst,
                           bool vec, hipStream_t stream);

@@ -125,5 +125,85 @@ __device__ __forceinline__ uint32_t chunk_abs_max(const Chunk<SRC_BF16>& c) {
   }
 }
 
+// ---- stochastic rounding ("Rounding: RNE versus stochastic rounding": between the
+//      neighbouring representable values l <= |a| < u, round up with probability
+//      (|a| - l) / (u - l); representable values stay)
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3",
+// SC 2011): ten rounds of two 32x32 -> 64-bit products (multipliers 0xD2511F53 and
+// 0xCD9E8D57) whose high halves are xored with the other counter words and the key, the
+// key bumped by 0x9E3779B9 / 0xBB67AE85 between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = c[0] * 0xD2511F53u, hi0 = __umulhi(c[0], 0xD2511F53u);
+    const uint32_t lo1 = c[2] * 0xCD9E8D57u, hi1 = __umulhi(c[2], 0xCD9E8D57u);
+    const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// The 24-bit random integers of the 32 elements of block b of line l, whose indices in
+// the padded code array are n = (l * nb + b) * 32 + j: element j takes word j % 4 of
+// Philox4x32-10(counter = (n / 4 low, n / 4 high, 0, 0), key = seed), top 24 bits.
+__device__ __forceinline__ void block_random24(uint64_t block_index, uint64_t seed, uint32_t r[32]) {
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const uint64_t ctr = block_index * 8u + (uint64_t)g;
+    uint32_t c[4] = {(uint32_t)ctr, (uint32_t)(ctr >> 32), 0u, 0u};
+    philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) r[4 * g + w] = c[w] >> 8;
+  }
+}
+
+// Stochastically rounded FP8 code of the value with fp32 bit pattern vb in a block with
+// finite scale byte sb (0..254), under the 24-bit random integer r: up iff r < 2^24 * p.
+// Everything is integer arithmetic on |v| = M * 2^(ev - 150) (M < 2^24), so the decision
+// is exact even where |v| / S would underflow in fp32: with the FP8 spacing 2^s of the
+// interval holding a = v / S, q = |a| / 2^s = M * 2^sh; the floor code comes from the
+// integer part, p * 2^24 from the fraction.  The scale rule keeps |a| <= fmax.
+template <int F>
+__device__ __forceinline__ uint32_t encode_sr(uint32_t vb, uint32_t sb, uint32_t r) {
+  constexpr int MB = F == kE4M3 ? 3 : 2;            // mantissa bits
+  constexpr int BIAS = F == kE4M3 ? 7 : 15;
+  constexpr int EMIN = 1 - BIAS;                    // exponent of the smallest normal
+  const uint32_t sign = (vb >> 24) & 0x80u;
+  const uint32_t mag = vb & 0x7FFFFFFFu;
+  if (mag == 0u) return sign;
+  const int e = (int)sb - 127;
+  const int ev0 = (int)(mag >> 23);
+  const uint32_t M = ev0 ? ((mag & 0x7FFFFFu) | 0x800000u) : (mag & 0x7FFFFFu);
+  const int ev = ev0 ? ev0 : 1;
+  const int lz = __clz((int)M) - 8;                 // leading zeros within 24 bits
+  const int xa = (23 - lz) + ev - 150 - e;          // floor(log2 |a|)
+  const int s = xa >= EMIN ? xa - MB : EMIN - MB;   // spacing exponent of the interval
+  const int sh = ev - 150 - e - s;                  // q = M * 2^sh
+  uint32_t floor_code;
+  if (xa >= EMIN) {
+    const uint32_t mn = M << lz;                    // leading one at bit 23
+    floor_code = ((uint32_t)(xa + BIAS) << MB) | ((mn >> (23 - MB)) & ((1u << MB) - 1u));
+  } else {
+    floor_code = sh >= 0 ? (M << sh) : (sh > -32 ? (M >> -sh) : 0u);
+  }
+  uint32_t up = 0u;
+  if (sh < 0) {
+    const int k = -sh;                              // fraction bits of q
+    if (k <= 24) {
+      const uint32_t fr = M & ((1u << k) - 1u);     // frac * 2^k
+      up = r < (fr << (24 - k)) ? 1u : 0u;
+    } else {                                        // q < 1: frac * 2^24 = M / 2^(k - 24)
+      const int kk = k - 24;
+      up = kk >= 40 ? (r == 0u ? 1u : 0u) : (((uint64_t)r << kk) < (uint64_t)M ? 1u : 0u);
+    }
+  }
+  return sign | (floor_code + up);
+}
+
 }  // namespace mxblock
 }  // namespace mxq

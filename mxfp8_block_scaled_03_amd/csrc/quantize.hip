@@ -280,6 +280,128 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(const void* __restrict_
     __syncthreads();
   }
 }
+// Rowwise quantize with stochastically rounded codes: one lane per block as in
+// k_quant_rows; the block's scale byte is the RNE quantizer's, its 32 codes are drawn by
+// encode_sr with the block's Philox words (line l, block b -> block index l * nb + b).
+template <int SRC_BF16, int F, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_quant_rows_sr(const void* __restrict__ src, int64_t ld_src, int64_t K,
+                                                           int64_t nb, int64_t nblocks, uint8_t* __restrict__ codes,
+                                                           int64_t ld_codes, uint8_t* __restrict__ scales,
+                                                           int64_t ld_scales, uint64_t seed) {
+  constexpr int ES = SRC_BF16 ? 2 : 4;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < nblocks; g += stride) {
+    const int64_t row = g / nb, b = g - row * nb;
+    const char* line = reinterpret_cast<const char*>(src) + row * ld_src * ES;
+    Chunk<SRC_BF16> c[4];
+    uint32_t amax = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      load_chunk<SRC_BF16, VEC>(c[q], line, 32 * b + 8 * q, K);
+      const uint32_t a = chunk_abs_max<SRC_BF16>(c[q]);
+      amax = amax > a ? amax : a;
+    }
+    const uint32_t sb = scale_byte_from_amax<F>(amax);
+    uint32_t d[8];
+    if (sb == 255u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d[i] = 0x7F7F7F7Fu;
+    } else {
+      uint32_t r[32];
+      block_random24((uint64_t)g, seed, r);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int el = 4 * i + j;
+          w |= encode_sr<F>(value_bits<SRC_BF16>(c[el >> 3], el & 7), sb, r[el]) << (8 * j);
+        }
+        d[i] = w;
+      }
+    }
+    uint4* out = reinterpret_cast<uint4*>(codes + row * ld_codes + 32 * b);
+    out[0] = make_uint4(d[0], d[1], d[2], d[3]);
+    out[1] = make_uint4(d[4], d[5], d[6], d[7]);
+    scales[row * ld_scales + b] = (uint8_t)sb;
+  }
+}
+
+// Columnwise quantize with stochastically rounded codes: the tile scheme of k_quant_cols;
+// thread (column c, block kb) draws the Philox words of block index col * nb + b.
+template <int SRC_BF16, int F, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_quant_cols_sr(const void* __restrict__ src, int64_t rows, int64_t cols,
+                                                           int64_t ld_src, int64_t nb, uint8_t* __restrict__ codes,
+                                                           int64_t ld_codes, uint8_t* __restrict__ scales,
+                                                           int64_t ld_scales, uint64_t seed) {
+  typedef typename std::conditional<SRC_BF16, uint16_t, uint32_t>::type E;
+  constexpr int PW = kColTileCols * (int)sizeof(E) / 4 + 1;
+  __shared__ uint32_t tile[kColTileRows * PW];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kColTileCols;
+  const E* s = reinterpret_cast<const E*>(src);
+  for (int64_t ty = blockIdx.y; ty * kColTileRows < rows; ty += gridDim.y) {
+    const int64_t r0 = ty * kColTileRows;
+    constexpr int EPV = 16 / sizeof(E);
+    constexpr int PPR = kColTileCols / EPV;
+    for (int p = tid; p < kColTileRows * PPR; p += kThreads) {
+      const int tr = p / PPR, tc = (p % PPR) * EPV;
+      const int64_t r = r0 + tr, cc = c0 + tc;
+      uint32_t* dst = &tile[tr * PW + tc * (int)sizeof(E) / 4];
+      if (VEC && r < rows && cc + EPV <= cols) {
+        const uint4 v = *reinterpret_cast<const uint4*>(s + r * ld_src + cc);
+        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+      } else {
+        E e[EPV];
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) e[i] = (r < rows && cc + i < cols) ? s[r * ld_src + cc + i] : (E)0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if (SRC_BF16) dst[w] = (uint32_t)e[2 * w] | ((uint32_t)e[2 * w + 1] << 16);
+          else dst[w] = (uint32_t)e[w];
+        }
+      }
+    }
+    __syncthreads();
+    const int c = tid >> 2, kb = tid & 3;
+    const int64_t col = c0 + c, b = r0 / 32 + kb;
+    if (col < cols && b < nb) {
+      uint32_t amax = 0;
+      uint32_t v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int row = 32 * kb + i;
+        uint32_t x;
+        if (SRC_BF16) x = (uint32_t)reinterpret_cast<const uint16_t*>(tile)[row * PW * 2 + c] << 16;
+        else x = tile[row * PW + c];
+        v[i] = x;
+        const uint32_t a = x & 0x7FFFFFFFu;
+        amax = amax > a ? amax : a;
+      }
+      const uint32_t sb = scale_byte_from_amax<F>(amax);
+      uint32_t out[8];
+      if (sb == 255u) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) out[i] = 0x7F7F7F7Fu;
+      } else {
+        uint32_t rnd[32];
+        block_random24((uint64_t)col * (uint64_t)nb + (uint64_t)b, seed, rnd);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t w = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w |= encode_sr<F>(v[4 * i + j], sb, rnd[4 * i + j]) << (8 * j);
+          out[i] = w;
+        }
+      }
+      uint4* dst = reinterpret_cast<uint4*>(codes + col * ld_codes + 32 * b);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      scales[col * ld_scales + b] = (uint8_t)sb;
+    }
+    __syncthreads();
+  }
+}
 }  // namespace
 
 int device_cu_count() {
@@ -382,6 +504,50 @@ hipError_t launch_quant_dual(const void* src, int src_bf16, int64_t rows, int64_
   if (fmt == kE4M3)
     return quant_dual_t<0, kE4M3>(src, rows, cols, ld_src, rcodes, ld_rc, rscales, ld_rs, ccodes, ld_cc, cscales, ld_cs, vec, stream);
   return quant_dual_t<0, kE5M2>(src, rows, cols, ld_src, rcodes, ld_rc, rscales, ld_rs, ccodes, ld_cc, cscales, ld_cs, vec, stream);
+}
+
+template <int SRC_BF16, int F>
+static hipError_t quant_sr_t(const void* src, int64_t rows, int64_t cols, int64_t ld_src, bool colwise,
+                             uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec,
+                             uint64_t seed, hipStream_t stream) {
+  if (!colwise) {
+    const int64_t nb = (cols + 31) / 32, nblocks = rows * nb;
+    const int64_t wg_needed = (nblocks + kThreads - 1) / kThreads;
+    const int64_t cap = (int64_t)device_cu_count() * 256;
+    const int grid = (int)(wg_needed < cap ? wg_needed : cap);
+    if (vec)
+      hipLaunchKernelGGL((k_quant_rows_sr<SRC_BF16, F, true>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src, cols,
+                         nb, nblocks, codes, ld_codes, scales, ld_scales, seed);
+    else
+      hipLaunchKernelGGL((k_quant_rows_sr<SRC_BF16, F, false>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src,
+                         cols, nb, nblocks, codes, ld_codes, scales, ld_scales, seed);
+    return hipGetLastError();
+  }
+  const int64_t nb = (rows + 31) / 32;
+  const int64_t gx = (cols + kColTileCols - 1) / kColTileCols;
+  int64_t gy = (rows + kColTileRows - 1) / kColTileRows;
+  if (gy > 65535) gy = 65535;
+  if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (vec)
+    hipLaunchKernelGGL((k_quant_cols_sr<SRC_BF16, F, true>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
+                       stream, src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales, seed);
+  else
+    hipLaunchKernelGGL((k_quant_cols_sr<SRC_BF16, F, false>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
+                       stream, src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales, seed);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_sr(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, bool colwise,
+                           int fmt, uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec,
+                           uint64_t seed, hipStream_t stream) {
+  if (src_bf16) {
+    if (fmt == kE4M3)
+      return quant_sr_t<1, kE4M3>(src, rows, cols, ld_src, colwise, codes, ld_codes, scales, ld_scales, vec, seed, stream);
+    return quant_sr_t<1, kE5M2>(src, rows, cols, ld_src, colwise, codes, ld_codes, scales, ld_scales, vec, seed, stream);
+  }
+  if (fmt == kE4M3)
+    return quant_sr_t<0, kE4M3>(src, rows, cols, ld_src, colwise, codes, ld_codes, scales, ld_scales, vec, seed, stream);
+  return quant_sr_t<0, kE5M2>(src, rows, cols, ld_src, colwise, codes, ld_codes, scales, ld_scales, vec, seed, stream);
 }
 
 }  // namespace mxq

@@ -18,7 +18,7 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert {"mxq_quantize", "mxq_quantize_dual", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex",
+    assert {"mxq_quantize", "mxq_quantize_dual", "mxq_quantize_sr", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex",
             "mxq_status_string", "mxq_version"} <= set(declared_symbols())
 
 
@@ -68,6 +68,26 @@ def test_quantize_validation():
     # empty problems succeed without touching pointers
     assert q(rows=0, src=None, codes=None, scales=None) == 0
     assert q(cols=0, src=None, codes=None, scales=None) == 0
+
+
+def test_quantize_sr_validation():
+    def qs(**kw):
+        a = dict(src=FAKE, src_type=mxq.MXQ_BF16, rows=4, cols=64, ld_src=64, axis=mxq.MXQ_ROWWISE,
+                 elem=mxq.MXQ_E5M2, seed=2 ** 64 - 1, codes=FAKE, ld_codes=64, scales=FAKE, ld_scales=2)
+        a.update(kw)
+        return mxq.mxq_quantize_sr(a["src"], a["src_type"], a["rows"], a["cols"], a["ld_src"], a["axis"], a["elem"],
+                                   a["seed"], a["codes"], a["ld_codes"], a["scales"], a["ld_scales"], None)
+    assert qs(src_type=mxq.MXQ_E4M3) == -5
+    assert qs(elem=mxq.MXQ_F32) == -5
+    assert qs(axis=3) == -6
+    assert qs(rows=-1) == -2
+    assert qs(codes=None) == -1
+    assert qs(ld_codes=48) == -3
+    assert qs(ld_scales=1) == -3
+    assert qs(ld_codes=80 + 1) == -4
+    assert qs(src=FAKE + 1) == -4
+    assert qs(axis=mxq.MXQ_COLWISE, ld_codes=16) == -3
+    assert qs(rows=0, src=None, codes=None, scales=None) == 0
 
 
 def qd(**kw):
