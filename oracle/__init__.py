@@ -56,6 +56,9 @@ def lib():
         L.mxo_quantize_sr.restype = None
         L.mxo_quantize_sr.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_uint64,
                                       vp, i64, vp, i64]
+        L.mxo_quantize_scaled.restype = None
+        L.mxo_quantize_scaled.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp, i64,
+                                          vp, i64, vp, i64, vp, vp, i64]
         L.mxo_silu.restype = ctypes.c_double
         L.mxo_silu.argtypes = [ctypes.c_double]
         L.mxo_silu_array.restype = None
@@ -190,6 +193,30 @@ def quantize_sr(src: np.ndarray, fmt: str, seed: int, axis: int = 0):
         lib().mxo_quantize_sr(_ptr(src), _src_type(src), rows, cols, cols, axis, FMT[fmt], int(seed) & (2 ** 64 - 1),
                               _ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1])
     return codes[:, :Kp], scales[:, :Kp // 32]
+
+
+def quantize_scaled(src: np.ndarray, fmt: str, given_scales: np.ndarray, axis: int = 0):
+    """Quantize with caller-owned E8M0 scale bytes given_scales [L][nb] (RNE-satfinite codes).
+
+    Returns (codes [L][Kp], amax [L][nb] float32, clipped [L][nb] uint8, flushed [L][nb] uint8).
+    """
+    src = np.ascontiguousarray(src)
+    rows, cols = src.shape
+    L, K = (rows, cols) if axis == 0 else (cols, rows)
+    Kp = 32 * ((K + 31) // 32)
+    nb = Kp // 32
+    gs = np.ascontiguousarray(given_scales, dtype=np.uint8)
+    if gs.shape != (L, nb):
+        raise ValueError("given_scales must be [L][nb] = %r" % ((L, nb),))
+    codes = np.zeros((L, max(Kp, 1)), dtype=np.uint8)
+    amax = np.zeros((L, max(nb, 1)), dtype=np.float32)
+    clipped = np.zeros((L, max(nb, 1)), dtype=np.uint8)
+    flushed = np.zeros((L, max(nb, 1)), dtype=np.uint8)
+    if L > 0 and K > 0:
+        lib().mxo_quantize_scaled(_ptr(src), _src_type(src), rows, cols, cols, axis, FMT[fmt], _ptr(gs), nb,
+                                  _ptr(codes), codes.shape[1], _ptr(amax), amax.shape[1], _ptr(clipped),
+                                  _ptr(flushed), clipped.shape[1])
+    return codes[:, :Kp], amax[:, :nb], clipped[:, :nb], flushed[:, :nb]
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, fmt: str, K: int, out: str = "f32"):

@@ -34,6 +34,11 @@
  *     the 32-bit word n%4 of Philox4x32-10(counter = (n/4 low, n/4 high, 0, 0), key = seed);
  *     its top 24 bits r decide: round up iff r < 2^24 * (|a| - l) / (u - l).  The scale
  *     rule is unchanged.
+ *   - Caller-owned (delayed or stale) scales: codes are RNE-satfinite(x / S) with the given
+ *     S; NaN -> 0x7F, +-Inf -> +-fmax, a given scale byte 255 makes the block 0x7F; an
+ *     element counts as clipped when |x / S| > fmax and as flushed when x != 0 (finite)
+ *     and its code has magnitude 0; the exported block amax is max |x| over the real
+ *     elements (NaN if any is NaN).
  */
 #include <math.h>
 #include <stdint.h>
@@ -356,6 +361,58 @@ void mxo_quantize_sr(const void *src, int src_type, int64_t rows, int64_t cols, 
                      uint8_t *scales, int64_t ld_scales)
 {
     quantize_any(src, src_type, rows, cols, ld_src, axis, fmt, codes, ld_codes, scales, ld_scales, 1, seed);
+}
+
+/* Quantize with caller-owned scale bytes [LPGP "Worked failure: stale delayed scale": a
+ * scale from an earlier amax saturates a later spike; "Delayed scaling in Transformer
+ * Engine": the quantization pass also records the current amax for the next scale
+ * update].  given_scales [L][ld_given]; optional per-block outputs (NULL = not written):
+ * amax [L][ld_amax] (FP32 max |x|), clipped and flushed counts [L][ld_diag].           */
+void mxo_quantize_scaled(const void *src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
+                         int axis, int fmt, const uint8_t *given_scales, int64_t ld_given,
+                         uint8_t *codes, int64_t ld_codes, float *amax_out, int64_t ld_amax,
+                         uint8_t *clipped, uint8_t *flushed, int64_t ld_diag)
+{
+    build_tables();
+    int64_t L = axis == 0 ? rows : cols;
+    int64_t K = axis == 0 ? cols : rows;
+    int64_t nb = (K + 31) / 32;
+    double fmax = mxo_fmax(fmt);
+    #pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t l = 0; l < L; ++l) {
+        int64_t base = axis == 0 ? l * ld_src : l;
+        int64_t stride = axis == 0 ? 1 : ld_src;
+        for (int64_t b = 0; b < nb; ++b) {
+            int sb = given_scales[l * ld_given + b];
+            double amax = 0.0;
+            int any_nan = 0, nclip = 0, nflush = 0;
+            for (int64_t k = 32 * b; k < 32 * b + 32; ++k) {
+                uint8_t c = 0x00;                                  /* zero padding */
+                if (k < K) {
+                    double x = load_elem(src, src_type, base + k * stride);
+                    if (isnan(x)) any_nan = 1;
+                    else if (fabs(x) > amax) amax = fabs(x);
+                    if (sb == 255 || isnan(x)) {
+                        c = 0x7F;
+                    } else {
+                        double a = ldexp(x, 127 - sb);             /* x / S, exact in FP64 */
+                        if (fabs(a) > fmax) {
+                            ++nclip;
+                            a = a < 0 ? -fmax : fmax;              /* saturate */
+                        }
+                        c = mxo_encode(a, fmt);
+                        if (x != 0.0 && (c & 0x7F) == 0) ++nflush;
+                    }
+                } else if (sb == 255) {
+                    c = 0x7F;
+                }
+                codes[l * ld_codes + k] = c;
+            }
+            if (amax_out) amax_out[l * ld_amax + b] = any_nan ? NAN : (float)amax;
+            if (clipped) clipped[l * ld_diag + b] = (uint8_t)nclip;
+            if (flushed) flushed[l * ld_diag + b] = (uint8_t)nflush;
+        }
+    }
 }
 
 /* ---------------------------------------------------------------- dequantize ------ */
