@@ -138,6 +138,29 @@ int mxq_quantize_sr(const void* src, int src_type, int64_t rows, int64_t cols, i
                     uint8_t* scales, int64_t ld_scales, void* stream);
 
 /*
+ * mxq_quantize_scaled -- quantize with caller-owned scale bytes, plus diagnostics.
+ * ("Worked failure: stale delayed scale": a scale taken from an earlier amax saturates a
+ * later spike into a finite, wrong value; "Delayed scaling in Transformer Engine": the
+ * quantization pass also records the current amax for the next scale update.)
+ *
+ * src, axis, elem, codes, ld_codes: as mxq_quantize.  scales [L][ld_scales] (ld >= nb) are
+ * INPUT E8M0 bytes chosen by the caller (delayed, stale or any other policy).  Codes are
+ * RNE-satfinite(x / S): |x / S| > fmax saturates to +-fmax (a clip), +-Inf too, NaN gives
+ * 0x7F, a scale byte of 255 makes the whole block 0x7F, pad codes are 0x00.  Optional
+ * per-block outputs (NULL = not written):
+ *   amax    [L][ld_amax] FP32 (4-byte aligned): max |x| over the block's real elements
+ *           (NaN if one is NaN) -- the value a delayed-scaling history records;
+ *   clipped [L][ld_diag] uint8: elements with |x / S| > fmax;
+ *   flushed [L][ld_diag] uint8: nonzero finite elements whose code is +-0.
+ * With the scale bytes mxq_quantize would choose, the codes equal mxq_quantize's and
+ * nothing is clipped.
+ */
+int mxq_quantize_scaled(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
+                        int axis, int elem, const uint8_t* scales, int64_t ld_scales,
+                        uint8_t* codes, int64_t ld_codes, float* amax, int64_t ld_amax,
+                        uint8_t* clipped, uint8_t* flushed, int64_t ld_diag, void* stream);
+
+/*
  * mxq_quantize_dual -- both orientations of one matrix from a single read of it.
  * ("Microscaling: the two-row experiment", closing paragraph: moving from 1x32 to 32x1
  * groups changes which values share a scale, so the second orientation is derived from

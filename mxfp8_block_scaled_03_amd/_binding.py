@@ -46,6 +46,8 @@ def lib():
         L.mxq_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, vp, i64, vp, i64, vp]
         L.mxq_quantize_sr.restype = ci
         L.mxq_quantize_sr.argtypes = [vp, ci, i64, i64, i64, ci, ci, ctypes.c_uint64, vp, i64, vp, i64, vp]
+        L.mxq_quantize_scaled.restype = ci
+        L.mxq_quantize_scaled.argtypes = [vp, ci, i64, i64, i64, ci, ci, vp, i64, vp, i64, vp, i64, vp, vp, i64, vp]
         L.mxq_quantize_dual.restype = ci
         L.mxq_quantize_dual.argtypes = [vp, ci, i64, i64, i64, ci, vp, i64, vp, i64, vp, i64, vp, i64, vp]
         L.mxq_dequantize.restype = ci
@@ -76,6 +78,12 @@ def mxq_quantize_sr(src, src_type, rows, cols, ld_src, axis, elem, seed, codes, 
                     stream=None) -> int:
     return lib().mxq_quantize_sr(src, src_type, rows, cols, ld_src, axis, elem, seed, codes, ld_codes, scales,
                                  ld_scales, stream)
+
+
+def mxq_quantize_scaled(src, src_type, rows, cols, ld_src, axis, elem, scales, ld_scales, codes, ld_codes,
+                        amax, ld_amax, clipped, flushed, ld_diag, stream=None) -> int:
+    return lib().mxq_quantize_scaled(src, src_type, rows, cols, ld_src, axis, elem, scales, ld_scales, codes,
+                                     ld_codes, amax, ld_amax, clipped, flushed, ld_diag, stream)
 
 
 def mxq_quantize_dual(src, src_type, rows, cols, ld_src, elem, row_codes, ld_row_codes, row_scales, ld_row_scales,
@@ -190,6 +198,36 @@ def quantize_sr(x, seed: int, elem: str = "e5m2", axis: str = "row", codes=None,
                          codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0), _stream_handle())
     _check(st, "mxq_quantize_sr")
     return codes, scales
+
+
+def quantize_scaled(x, scales, elem: str = "e4m3", axis: str = "row", diagnostics: bool = True):
+    """Quantize with caller-owned E8M0 scale bytes `scales` [L][nb] (uint8 CUDA tensor).
+
+    Returns codes [L][Kp], or (codes, amax [L][nb] float32, clipped [L][nb] uint8,
+    flushed [L][nb] uint8) with diagnostics=True (see mxq_quantize_scaled)."""
+    torch = _torch()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("quantize_scaled expects a 2-D tensor with unit stride along the last dimension")
+    rows, cols = x.shape
+    L, K = (rows, cols) if axis == "row" else (cols, rows)
+    Kp = _round_up(K, 32)
+    nb = Kp // 32
+    if scales.dtype != torch.uint8 or tuple(scales.shape) != (L, nb) or (L > 0 and scales.stride(1) != 1):
+        raise ValueError("scales must be a uint8 [L][nb] tensor with unit inner stride")
+    codes = torch.empty((L, Kp), dtype=torch.uint8, device=x.device)
+    amax = clipped = flushed = None
+    if diagnostics:
+        amax = torch.empty((L, nb), dtype=torch.float32, device=x.device)
+        clipped = torch.empty((L, nb), dtype=torch.uint8, device=x.device)
+        flushed = torch.empty((L, nb), dtype=torch.uint8, device=x.device)
+    st = mxq_quantize_scaled(x.data_ptr(), _wide_type(x), rows, cols, x.stride(0) if rows > 0 else cols,
+                             MXQ_ROWWISE if axis == "row" else MXQ_COLWISE, _ELEM[elem], scales.data_ptr(),
+                             scales.stride(0) if L > 0 else nb, codes.data_ptr(), codes.stride(0),
+                             None if amax is None else amax.data_ptr(), nb,
+                             None if clipped is None else clipped.data_ptr(),
+                             None if flushed is None else flushed.data_ptr(), nb, _stream_handle())
+    _check(st, "mxq_quantize_scaled")
+    return (codes, amax, clipped, flushed) if diagnostics else codes
 
 
 def quantize_dual(x, elem: str = "e4m3"):

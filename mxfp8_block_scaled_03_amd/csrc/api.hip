@@ -93,6 +93,35 @@ int mxq_quantize_sr(const void* src, int src_type, int64_t rows, int64_t cols, i
                                          (hipStream_t)stream));
 }
 
+int mxq_quantize_scaled(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int axis,
+                        int elem, const uint8_t* scales, int64_t ld_scales, uint8_t* codes, int64_t ld_codes,
+                        float* amax, int64_t ld_amax, uint8_t* clipped, uint8_t* flushed, int64_t ld_diag,
+                        void* stream) {
+  if (!is_wide(src_type) || !is_elem(elem)) return MXQ_ERR_DTYPE;
+  if (axis != MXQ_ROWWISE && axis != MXQ_COLWISE) return MXQ_ERR_ARG;
+  if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return MXQ_ERR_SHAPE;
+  const int64_t L = axis == MXQ_ROWWISE ? rows : cols;
+  const int64_t K = axis == MXQ_ROWWISE ? cols : rows;
+  const int64_t Kp = 32 * ((K + 31) / 32), nb = Kp / 32;
+  if (L == 0 || K == 0) return MXQ_OK;
+  if (!src || !codes || !scales) return MXQ_ERR_NULL;
+  const int64_t es = src_type == MXQ_BF16 ? 2 : 4;
+  if (ld_src < cols || ld_codes < Kp || ld_scales < nb) return MXQ_ERR_LD;
+  if (amax && ld_amax < nb) return MXQ_ERR_LD;
+  if ((clipped || flushed) && ld_diag < nb) return MXQ_ERR_LD;
+  if (!mul_ok(rows, ld_src * es) || !mul_ok(L, ld_codes) || !mul_ok(L, ld_scales) ||
+      (amax && !mul_ok(L, ld_amax * 4)) || ((clipped || flushed) && !mul_ok(L, ld_diag)))
+    return MXQ_ERR_SHAPE;
+  if (!aligned(src, (uintptr_t)es) || !aligned(codes, 16) || ld_codes % 16 != 0 || (amax && !aligned(amax, 4)))
+    return MXQ_ERR_ALIGN;
+  const bool src16 = aligned(src, 16) && (ld_src * es) % 16 == 0;
+  const bool vec = axis == MXQ_ROWWISE ? (src16 && K % 8 == 0) : src16;
+  return hip_status(mxq::launch_quant_scaled(src, src_type == MXQ_BF16, rows, cols, ld_src, axis == MXQ_COLWISE,
+                                             to_fmt(elem), scales, ld_scales, codes, ld_codes, amax,
+                                             amax ? ld_amax : 0, clipped, flushed, (clipped || flushed) ? ld_diag : 0,
+                                             vec, (hipStream_t)stream));
+}
+
 int mxq_quantize_dual(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int elem,
                       uint8_t* row_codes, int64_t ld_row_codes, uint8_t* row_scales, int64_t ld_row_scales,
                       uint8_t* col_codes, int64_t ld_col_codes, uint8_t* col_scales, int64_t ld_col_scales,

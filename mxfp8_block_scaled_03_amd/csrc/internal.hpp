@@ -34,6 +34,13 @@ hipError_t launch_quant_sr(const void* src, int src_bf16, int64_t rows, int64_t 
                            int fmt, uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec,
                            uint64_t seed, hipStream_t stream);
 
+// Quantize with caller-owned scale bytes given [L][ld_given] (RNE-satfinite codes) and
+// optional per-block diagnostics: amax (fp32), clipped and flushed counts (null = skip).
+hipError_t launch_quant_scaled(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, bool colwise,
+                               int fmt, const uint8_t* given, int64_t ld_given, uint8_t* codes, int64_t ld_codes,
+                               float* amax, int64_t ld_amax, uint8_t* clipped, uint8_t* flushed, int64_t ld_diag,
+                               bool vec, hipStream_t stream);
+
 hipError_t launch_dequant(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales, int64_t ld_scales,
                           int fmt, int64_t L, int64_t K, void* dst, int dst_bf16, int64_t ld_dst,
                           bool vec, hipStream_t stream);

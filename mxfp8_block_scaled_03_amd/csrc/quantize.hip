@@ -402,6 +402,142 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols_sr(const void* __restri
     __syncthreads();
   }
 }
+// Codes of one 32-value block under a caller-owned scale byte sb ("Worked failure: stale
+// delayed scale"): RNE-satfinite(x / S) by the exact software encoder (x / S by ldexp,
+// exact unless it over- or underflows fp32, where the code is fmax or zero anyway), NaN ->
+// 0x7F, sb = 255 -> the whole block 0x7F.  Counts the elements saturated (|x / S| > fmax)
+// and the nonzero ones that become a zero code; returns the block's abs-max bit pattern.
+// n_real: elements of the block inside the line (the rest are padding, code 0x00).
+template <int F>
+__device__ __forceinline__ uint32_t encode_scaled_block(const uint32_t v[32], uint32_t sb, int n_real, uint32_t out[8],
+                                                        uint32_t& nclip, uint32_t& nflush) {
+  uint32_t amax = 0;
+  nclip = nflush = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int el = 4 * i + j;
+      const uint32_t x = v[el];
+      const uint32_t mag = x & 0x7FFFFFFFu;
+      uint32_t c = 0u;
+      if (el < n_real) {
+        amax = amax > mag ? amax : mag;
+        if (sb == 255u || mag > 0x7F800000u) {
+          c = 0x7Fu;
+        } else {
+          const float a = ldexpf(__uint_as_float(x), 127 - (int)sb);
+          const bool clip = (__float_as_uint(a) & 0x7FFFFFFFu) > Fp8<F>::max_bits;
+          c = encode_rne_sat<F>(a);
+          nclip += clip ? 1u : 0u;
+          nflush += (mag != 0u && (c & 0x7Fu) == 0u) ? 1u : 0u;
+        }
+      } else if (sb == 255u) {
+        c = 0x7Fu;
+      }
+      w |= c << (8 * j);
+    }
+    out[i] = w;
+  }
+  return amax;
+}
+
+// Rowwise quantize with caller-owned scale bytes: one lane per block.
+template <int SRC_BF16, int F, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_quant_rows_scaled(
+    const void* __restrict__ src, int64_t ld_src, int64_t K, int64_t nb, int64_t nblocks,
+    const uint8_t* __restrict__ given, int64_t ld_given, uint8_t* __restrict__ codes, int64_t ld_codes,
+    float* __restrict__ amax_out, int64_t ld_amax, uint8_t* __restrict__ clipped, uint8_t* __restrict__ flushed,
+    int64_t ld_diag) {
+  constexpr int ES = SRC_BF16 ? 2 : 4;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < nblocks; g += stride) {
+    const int64_t row = g / nb, b = g - row * nb;
+    const char* line = reinterpret_cast<const char*>(src) + row * ld_src * ES;
+    Chunk<SRC_BF16> c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_chunk<SRC_BF16, VEC>(c[q], line, 32 * b + 8 * q, K);
+    uint32_t v[32];
+#pragma unroll
+    for (int el = 0; el < 32; ++el) v[el] = value_bits<SRC_BF16>(c[el >> 3], el & 7);
+    const int64_t rem = K - 32 * b;
+    const int n_real = rem < 32 ? (int)rem : 32;
+    const uint32_t sb = given[row * ld_given + b];
+    uint32_t d[8], nclip, nflush;
+    const uint32_t amax = F == kE4M3 ? encode_scaled_block<kE4M3>(v, sb, n_real, d, nclip, nflush)
+                                     : encode_scaled_block<kE5M2>(v, sb, n_real, d, nclip, nflush);
+    uint4* out = reinterpret_cast<uint4*>(codes + row * ld_codes + 32 * b);
+    out[0] = make_uint4(d[0], d[1], d[2], d[3]);
+    out[1] = make_uint4(d[4], d[5], d[6], d[7]);
+    if (amax_out) amax_out[row * ld_amax + b] = __uint_as_float(amax);
+    if (clipped) clipped[row * ld_diag + b] = (uint8_t)nclip;
+    if (flushed) flushed[row * ld_diag + b] = (uint8_t)nflush;
+  }
+}
+
+// Columnwise quantize with caller-owned scale bytes: the tile scheme of k_quant_cols.
+template <int SRC_BF16, int F, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_quant_cols_scaled(
+    const void* __restrict__ src, int64_t rows, int64_t cols, int64_t ld_src, int64_t nb,
+    const uint8_t* __restrict__ given, int64_t ld_given, uint8_t* __restrict__ codes, int64_t ld_codes,
+    float* __restrict__ amax_out, int64_t ld_amax, uint8_t* __restrict__ clipped, uint8_t* __restrict__ flushed,
+    int64_t ld_diag) {
+  typedef typename std::conditional<SRC_BF16, uint16_t, uint32_t>::type E;
+  constexpr int PW = kColTileCols * (int)sizeof(E) / 4 + 1;
+  __shared__ uint32_t tile[kColTileRows * PW];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kColTileCols;
+  const E* s = reinterpret_cast<const E*>(src);
+  for (int64_t ty = blockIdx.y; ty * kColTileRows < rows; ty += gridDim.y) {
+    const int64_t r0 = ty * kColTileRows;
+    constexpr int EPV = 16 / sizeof(E);
+    constexpr int PPR = kColTileCols / EPV;
+    for (int p = tid; p < kColTileRows * PPR; p += kThreads) {
+      const int tr = p / PPR, tc = (p % PPR) * EPV;
+      const int64_t r = r0 + tr, cc = c0 + tc;
+      uint32_t* dst = &tile[tr * PW + tc * (int)sizeof(E) / 4];
+      if (VEC && r < rows && cc + EPV <= cols) {
+        const uint4 v = *reinterpret_cast<const uint4*>(s + r * ld_src + cc);
+        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+      } else {
+        E e[EPV];
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) e[i] = (r < rows && cc + i < cols) ? s[r * ld_src + cc + i] : (E)0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if (SRC_BF16) dst[w] = (uint32_t)e[2 * w] | ((uint32_t)e[2 * w + 1] << 16);
+          else dst[w] = (uint32_t)e[w];
+        }
+      }
+    }
+    __syncthreads();
+    const int c = tid >> 2, kb = tid & 3;
+    const int64_t col = c0 + c, b = r0 / 32 + kb;
+    if (col < cols && b < nb) {
+      uint32_t v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int row = 32 * kb + i;
+        if (SRC_BF16) v[i] = (uint32_t)reinterpret_cast<const uint16_t*>(tile)[row * PW * 2 + c] << 16;
+        else v[i] = tile[row * PW + c];
+      }
+      const int64_t rem = rows - 32 * b;
+      const int n_real = rem < 32 ? (int)rem : 32;
+      const uint32_t sb = given[col * ld_given + b];
+      uint32_t out[8], nclip, nflush;
+      const uint32_t amax = F == kE4M3 ? encode_scaled_block<kE4M3>(v, sb, n_real, out, nclip, nflush)
+                                       : encode_scaled_block<kE5M2>(v, sb, n_real, out, nclip, nflush);
+      uint4* dst = reinterpret_cast<uint4*>(codes + col * ld_codes + 32 * b);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      if (amax_out) amax_out[col * ld_amax + b] = __uint_as_float(amax);
+      if (clipped) clipped[col * ld_diag + b] = (uint8_t)nclip;
+      if (flushed) flushed[col * ld_diag + b] = (uint8_t)nflush;
+    }
+    __syncthreads();
+  }
+}
 }  // namespace
 
 int device_cu_count() {
@@ -535,6 +671,58 @@ static hipError_t quant_sr_t(const void* src, int64_t rows, int64_t cols, int64_
     hipLaunchKernelGGL((k_quant_cols_sr<SRC_BF16, F, false>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
                        stream, src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales, seed);
   return hipGetLastError();
+}
+
+template <int SRC_BF16, int F>
+static hipError_t quant_scaled_t(const void* src, int64_t rows, int64_t cols, int64_t ld_src, bool colwise,
+                                 const uint8_t* given, int64_t ld_given, uint8_t* codes, int64_t ld_codes,
+                                 float* amax, int64_t ld_amax, uint8_t* clipped, uint8_t* flushed, int64_t ld_diag,
+                                 bool vec, hipStream_t stream) {
+  if (!colwise) {
+    const int64_t nb = (cols + 31) / 32, nblocks = rows * nb;
+    const int64_t wg_needed = (nblocks + kThreads - 1) / kThreads;
+    const int64_t cap = (int64_t)device_cu_count() * 256;
+    const int grid = (int)(wg_needed < cap ? wg_needed : cap);
+    if (vec)
+      hipLaunchKernelGGL((k_quant_rows_scaled<SRC_BF16, F, true>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src,
+                         cols, nb, nblocks, given, ld_given, codes, ld_codes, amax, ld_amax, clipped, flushed, ld_diag);
+    else
+      hipLaunchKernelGGL((k_quant_rows_scaled<SRC_BF16, F, false>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src,
+                         cols, nb, nblocks, given, ld_given, codes, ld_codes, amax, ld_amax, clipped, flushed, ld_diag);
+    return hipGetLastError();
+  }
+  const int64_t nb = (rows + 31) / 32;
+  const int64_t gx = (cols + kColTileCols - 1) / kColTileCols;
+  int64_t gy = (rows + kColTileRows - 1) / kColTileRows;
+  if (gy > 65535) gy = 65535;
+  if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (vec)
+    hipLaunchKernelGGL((k_quant_cols_scaled<SRC_BF16, F, true>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
+                       stream, src, rows, cols, ld_src, nb, given, ld_given, codes, ld_codes, amax, ld_amax, clipped,
+                       flushed, ld_diag);
+  else
+    hipLaunchKernelGGL((k_quant_cols_scaled<SRC_BF16, F, false>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0,
+                       stream, src, rows, cols, ld_src, nb, given, ld_given, codes, ld_codes, amax, ld_amax, clipped,
+                       flushed, ld_diag);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_scaled(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, bool colwise,
+                               int fmt, const uint8_t* given, int64_t ld_given, uint8_t* codes, int64_t ld_codes,
+                               float* amax, int64_t ld_amax, uint8_t* clipped, uint8_t* flushed, int64_t ld_diag,
+                               bool vec, hipStream_t stream) {
+  if (src_bf16) {
+    if (fmt == kE4M3)
+      return quant_scaled_t<1, kE4M3>(src, rows, cols, ld_src, colwise, given, ld_given, codes, ld_codes, amax, ld_amax,
+                                      clipped, flushed, ld_diag, vec, stream);
+    return quant_scaled_t<1, kE5M2>(src, rows, cols, ld_src, colwise, given, ld_given, codes, ld_codes, amax, ld_amax,
+                                    clipped, flushed, ld_diag, vec, stream);
+  }
+  if (fmt == kE4M3)
+    return quant_scaled_t<0, kE4M3>(src, rows, cols, ld_src, colwise, given, ld_given, codes, ld_codes, amax, ld_amax,
+                                    clipped, flushed, ld_diag, vec, stream);
+  return quant_scaled_t<0, kE5M2>(src, rows, cols, ld_src, colwise, given, ld_given, codes, ld_codes, amax, ld_amax,
+                                  clipped, flushed, ld_diag, vec, stream);
 }
 
 hipError_t launch_quant_sr(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, bool colwise,

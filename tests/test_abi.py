@@ -18,7 +18,7 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert {"mxq_quantize", "mxq_quantize_dual", "mxq_quantize_sr", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex",
+    assert {"mxq_quantize", "mxq_quantize_dual", "mxq_quantize_sr", "mxq_quantize_scaled", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex",
             "mxq_status_string", "mxq_version"} <= set(declared_symbols())
 
 
@@ -88,6 +88,28 @@ def test_quantize_sr_validation():
     assert qs(src=FAKE + 1) == -4
     assert qs(axis=mxq.MXQ_COLWISE, ld_codes=16) == -3
     assert qs(rows=0, src=None, codes=None, scales=None) == 0
+
+
+def test_quantize_scaled_validation():
+    def qc(**kw):
+        a = dict(src=FAKE, src_type=mxq.MXQ_F32, rows=4, cols=64, ld_src=64, axis=mxq.MXQ_ROWWISE,
+                 elem=mxq.MXQ_E4M3, scales=FAKE, ld_scales=2, codes=FAKE, ld_codes=64, amax=None, ld_amax=0,
+                 clipped=None, flushed=None, ld_diag=0)
+        a.update(kw)
+        return mxq.mxq_quantize_scaled(a["src"], a["src_type"], a["rows"], a["cols"], a["ld_src"], a["axis"],
+                                       a["elem"], a["scales"], a["ld_scales"], a["codes"], a["ld_codes"], a["amax"],
+                                       a["ld_amax"], a["clipped"], a["flushed"], a["ld_diag"], None)
+    assert qc(elem=mxq.MXQ_BF16) == -5
+    assert qc(axis=2) == -6
+    assert qc(scales=None) == -1
+    assert qc(ld_scales=1) == -3
+    assert qc(amax=FAKE, ld_amax=1) == -3
+    assert qc(clipped=FAKE, ld_diag=1) == -3
+    assert qc(flushed=FAKE, ld_diag=1) == -3
+    assert qc(amax=FAKE + 2, ld_amax=2) == -4
+    assert qc(codes=FAKE + 4) == -4
+    assert qc(src=FAKE + 2) == -4
+    assert qc(cols=0, src=None, scales=None, codes=None) == 0
 
 
 def qd(**kw):
