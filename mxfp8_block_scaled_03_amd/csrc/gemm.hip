@@ -517,7 +517,7 @@ constexpr int kEpiWaveBytes = 16384;            // per-wave epilogue staging (in
 __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, v4i rsrc) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -590,18 +590,20 @@ __device__ __forceinline__ void issue_code(const Dma& d, const StepDma& sd, int 
 // which orders it after the last reader of `after` and before the first reader of
 // `before` without any hardware dependency.  (Only operands are named: naming an MFMA
 // result would make the compiler copy it while the MFMA is still writing it.)
-__device__ __forceinline__ void dma16_between(uint32_t lds, uint32_t voff, v4i rsrc, v8i& after, v8i& before) {
+template <typename V>
+__device__ __forceinline__ void dma16_between(uint32_t lds, uint32_t voff, v4i rsrc, V& after, V& before) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %3, %4, 0 offen lds"
                : "+v"(after), "+v"(before)
-               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
 
 // The same after the last MFMA that reads `after`.
-__device__ __forceinline__ void dma16_after(uint32_t lds, uint32_t voff, v4i rsrc, v8i& after) {
+template <typename V>
+__device__ __forceinline__ void dma16_after(uint32_t lds, uint32_t voff, v4i rsrc, V& after) {
   asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
                : "+v"(after)
-               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -626,7 +628,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool EXACT>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, int tiles_m, int tiles_n,
                                                         const uint8_t* __restrict__ xc, int64_t ld_x,
                                                         const uint8_t* __restrict__ xs, int64_t ld_xs,
@@ -718,6 +720,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
 
   v8i fa[4], fb[2];
   uint32_t sa[4], sb[2];
+  // exact-product mode: bf16 operands of one half step (bits of v8bf), [fragment][MFMA]
+  v4i ea[4][2], eb[2][2];
 
   // memory phase of step s: fragments and scales of step s, then wait for this wave's DMA
   // of step s+1 (its LDS reads complete at the barrier that follows); only the DMA of step
@@ -805,6 +809,100 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
       }
   };
 
+  // Exact-product mode.  A step is split into two halves: half h holds the 16-byte half h
+  // of every fragment row, i.e. block 2s + h of the step (lane g's half h covers k = 32h +
+  // 16g .. +15 of the 64-byte step).  Its memory phase reads those halves, decodes them
+  // with the block's scale to bf16 (exact while code * 2^(s-127) lies in bf16's range) and
+  // its compute phase runs 16 v_mfma_f32_32x32x16_bf16: MFMA m of a fragment takes bytes
+  // 8m..8m+7 of every lane, the same k for W and X, so each MFMA contracts 16 matching k
+  // of one block with exact products and FP32 sums.  The DMA and the waits are those of
+  // the matrix-core mode (issued in half 0, waited in half 0).
+  auto memory_half = [&](int s, auto h_c, auto par, auto last) __attribute__((always_inline)) {
+    constexpr int h = decltype(h_c)::value;
+    const uint32_t so = (uint32_t)(s & 3) * kStageBytes;
+    v4i ca[4], cb[2];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) ca[f] = lds16(ra[h] + so, 2048 * f);
+#pragma unroll
+    for (int f = 0; f < 2; ++f) cb[f] = lds16(rb[h] + so, 2048 * f);
+    // scale dwords of blocks 4u..4u+3 (u = s/2) of each fragment row, read at the first half
+    // of even steps and kept for the odd one; block 2s + h is byte 2(s&1) + h
+    if (h == 0 && decltype(par)::value == 0) {
+      const uint32_t ss = (uint32_t)((s >> 3) & 1) * kScaleSlot + 4u * (uint32_t)((s & 7) >> 1);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) sa[f] = *reinterpret_cast<const uint32_t*>(smem + rsa + ss + 512 * f);
+#pragma unroll
+      for (int f = 0; f < 2; ++f) sb[f] = *reinterpret_cast<const uint32_t*>(smem + rsb + ss + 512 * f);
+    }
+    bool dead_block = false;
+    if (decltype(last)::value) {
+      if ((K & 63) != 0) {
+        // dword e of this half holds k = 64s + 32h + 16g + 4e .. +3
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int keep = K - (64 * s + 32 * h + 16 * lg + 4 * e);
+          const uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
+#pragma unroll
+          for (int f = 0; f < 4; ++f) ca[f][e] = (int)((uint32_t)ca[f][e] & m);
+#pragma unroll
+          for (int f = 0; f < 2; ++f) cb[f][e] = (int)((uint32_t)cb[f][e] & m);
+        }
+      }
+      dead_block = 2 * s + h >= nb;   // its bytes are zero; its scale byte is not read
+    }
+    const uint32_t sh = 8u * (uint32_t)(2 * (s & 1) + h);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const float sc = e8m0_to_f32(dead_block ? 127u : (sa[f] >> sh) & 0xFFu);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        ea[f][m] = __builtin_bit_cast(v4i, codes_to_bf16<FA>((uint32_t)ca[f][2 * m], (uint32_t)ca[f][2 * m + 1], sc));
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const float sc = e8m0_to_f32(dead_block ? 127u : (sb[f] >> sh) & 0xFFu);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        eb[f][m] = __builtin_bit_cast(v4i, codes_to_bf16<FB>((uint32_t)cb[f][2 * m], (uint32_t)cb[f][2 * m + 1], sc));
+    }
+    if (h == 0) {
+      if (decltype(last)::value)
+        wait_vm<0>();
+      else
+        wait_vm<kLoadsPerStep>();
+    }
+  };
+
+  // Compute phase of one half step: 16 bf16 MFMAs (both MFMAs of every tile, the first of
+  // each tile before any second one), with the DMA of step s+3 issued between the first
+  // eight in half 0 as in the matrix-core mode.
+  auto compute_half = [&](int s, auto with_dma) __attribute__((always_inline)) {
+    constexpr bool DMA = decltype(with_dma)::value;
+    StepDma sd;
+    if (DMA) {
+      sd = step_dma(d, s + 3);
+      issue_scales(d, s + 3);
+    }
+    asm volatile("" : "+v"(ea[0][0]), "+v"(ea[1][0]), "+v"(ea[2][0]), "+v"(ea[3][0]), "+v"(eb[0][0]), "+v"(eb[1][0]));
+    asm volatile("" : "+v"(ea[0][1]), "+v"(ea[1][1]), "+v"(ea[2][1]), "+v"(ea[3][1]), "+v"(eb[0][1]), "+v"(eb[1][1]));
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < 2; ++fj) {
+          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, eb[fj][m]),
+                                                                __builtin_bit_cast(v8bf, ea[fi][m]), acc[fi][fj], 0, 0, 0);
+          if (DMA && m == 0 && fj == 1 && fi < 3) {
+            const uint32_t lds = fi == 0 ? d.lds_a + sd.so : fi == 1 ? d.lds_a + sd.so + 1024 : d.lds_b + sd.so;
+            const uint32_t voff = fi == 0 ? d.voff_a0 : fi == 1 ? d.voff_a1 : d.voff_b0;
+            dma16_between(lds, voff, fi < 2 ? sd.ra : sd.rb, ea[fi][0], ea[fi + 1][0]);
+          }
+          if (DMA && m == 0 && fj == 1 && fi == 3)
+            dma16_after(d.lds_b + sd.so + 1024, d.voff_b1, sd.rb, ea[3][0]);
+        }
+  };
+
   // ---- prologue: steps 0..2 in flight, step 0 landed everywhere
 #pragma unroll
   for (int s = 0; s < 3; ++s)
@@ -831,22 +929,47 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
   using C1 = std::integral_constant<int, 1>;
   using No = std::false_type;
   using Yes = std::true_type;
+  // exact-product mode: two half steps, each a memory phase and a compute phase
+  auto step_exact = [&](int s, auto par, auto last) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    memory_half(s, C0(), par, last);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    compute_half(s, std::integral_constant<bool, !decltype(last)::value>());
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    memory_half(s, C1(), par, last);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    compute_half(s, No());
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+  };
+  auto any_step = [&](int s, auto par, auto last) __attribute__((always_inline)) {
+    if constexpr (EXACT)
+      step_exact(s, par, last);
+    else
+      step(s, par, last);
+  };
   // steps 0..T-2 in pairs (even step: opsel byte 0, odd: byte 2); the last step, which
   // may be partial, on its own
   int s = 0;
   for (; s + 2 <= T - 1; s += 2) {
-    step(s, C0(), No());
-    step(s + 1, C1(), No());
+    any_step(s, C0(), No());
+    any_step(s + 1, C1(), No());
   }
   if (s < T - 1) {
-    step(s, C0(), No());
+    any_step(s, C0(), No());
     ++s;
   }
   if (T > 0) {
     if (s & 1)
-      step(s, C1(), Yes());
+      any_step(s, C1(), Yes());
     else
-      step(s, C0(), Yes());
+      any_step(s, C0(), Yes());
   }
   if (gp == 0) lds_barrier();   // matches group 1's extra barrier: all LDS reads are done
 
@@ -994,12 +1117,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
   }
 }
 
-template <int FA, int FB>
+template <int FA, int FB, bool EXACT>
 hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
                     int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
                     const GemmEpilogue& ep, hipStream_t stream) {
   static bool attr_set[64] = {false};
-  auto kern = k_gemm_pp<FA, FB>;
+  auto kern = k_gemm_pp<FA, FB, EXACT>;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (!attr_set[dev]) {
@@ -1013,13 +1136,22 @@ hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t 
   return hipGetLastError();
 }
 
+template <bool EXACT>
+hipError_t launch_e(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
+                    int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, int w_fmt,
+                    const GemmEpilogue& ep, hipStream_t stream) {
+  if (x_fmt == kE4M3 && w_fmt == kE4M3)
+    return launch_f<0, 0, EXACT>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+  if (x_fmt == kE4M3) return launch_f<0, 1, EXACT>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+  if (w_fmt == kE4M3) return launch_f<1, 0, EXACT>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+  return launch_f<1, 1, EXACT>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+}
+
 hipError_t launch(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs, int64_t ld_xs,
                   int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws, int w_fmt,
-                  const GemmEpilogue& ep, hipStream_t stream) {
-  if (x_fmt == kE4M3 && w_fmt == kE4M3) return launch_f<0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
-  if (x_fmt == kE4M3) return launch_f<0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
-  if (w_fmt == kE4M3) return launch_f<1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
-  return launch_f<1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+                  const GemmEpilogue& ep, bool exact, hipStream_t stream) {
+  if (exact) return launch_e<true>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, ep, stream);
+  return launch_e<false>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, ep, stream);
 }
 
 }  // namespace pp
@@ -1063,7 +1195,8 @@ hipError_t launch_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64
   const int64_t ey = ep.y_bf16 ? 2 : 4;
   ep.y_vec16 = ep.y && ((uintptr_t)ep.y % 16 == 0) && ((ep.ld_y * ey) % 16 == 0);
   const bool scales16 = ((uintptr_t)xs % 16 == 0) && ((uintptr_t)ws % 16 == 0) && ld_xs % 16 == 0 && ld_ws % 16 == 0;
-  if (!exact && scales16) return pp::launch(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, ep, stream);
+  if (scales16)
+    return pp::launch(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, ep, exact != 0, stream);
   if (exact) return gemm_m<1>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, ep, stream);
   return gemm_m<0>(M, N, K, xc, ld_x, xs, ld_xs, x_fmt, wc, ld_w, ws, ld_ws, w_fmt, ep, stream);
 }

@@ -1,8 +1,8 @@
 """GPU parity of mxq_gemm_ex: the SiLU epilogue against the FP64 oracle's SiLU, and the
 producer-fused MX output (codes and scales of bf16(Y) along N, written by the GEMM's
 epilogue) against the oracle's quantize of the bf16 Y the same GEMM writes -- byte for
-byte, in both kernels (16-byte aligned scale rows: ping-pong kernel; other layouts and
-exact accumulation: the 4-wave kernel)."""
+byte, in both kernels and both accumulation modes (16-byte aligned scale rows: the
+ping-pong kernel; other layouts: the 4-wave kernel)."""
 import numpy as np
 import pytest
 import torch
@@ -19,7 +19,7 @@ DEV = "cuda:0"
 # value, plus an absolute floor for results below the normal range
 SILU_REL = 2.0 ** -20
 SILU_ABS = 2.0 ** -126
-PATHS = ["pingpong", "fallback", "exact"]
+PATHS = ["pingpong", "fallback", "pingpong_exact", "fallback_exact"]
 
 
 def operands(M, N, K, seed, path, xstd=1.0, wstd=0.02, bias=True):
@@ -29,7 +29,7 @@ def operands(M, N, K, seed, path, xstd=1.0, wstd=0.02, bias=True):
     w = torch.from_numpy(rng.standard_normal((N, Kq)).astype(np.float32) * np.float32(wstd)).to(DEV)
     xc, xs = mxq.quantize(x, "e4m3", "row")
     wc, ws = mxq.quantize(w, "e4m3", "row")
-    if path == "fallback":                      # odd scale pitch: the 4-wave kernel
+    if path.startswith("fallback"):             # odd scale pitch: the 4-wave kernel
         xs, ws = odd_pitch(xs), odd_pitch(ws)
     b = torch.from_numpy(rng.standard_normal(N).astype(np.float32) * 0.5).to(DEV) if bias else None
     return xc, xs, wc, ws, b
@@ -45,7 +45,7 @@ def odd_pitch(s):
 
 
 def accum_of(path):
-    return "fp32" if path == "exact" else "fp8"
+    return "fp32" if path.endswith("exact") else "fp8"
 
 
 @pytest.mark.parametrize("path", PATHS)

@@ -106,12 +106,13 @@ def strided_scales(s, ld, offset=0):
     return view
 
 
+@pytest.mark.parametrize("accum", ACCS)
 @pytest.mark.parametrize("layout", ["ld%16", "ld%4", "ld odd", "unaligned"])
 @pytest.mark.parametrize("M,N,K", [(300, 260, 4000), (257, 300, 96), (130, 70, 33), (64, 520, 4001)])
-def test_gemm_scale_layouts(M, N, K, layout):
+def test_gemm_scale_layouts(M, N, K, layout, accum):
     """Scale rows with a 16-byte aligned base and leading dimension take the ping-pong
-    kernel, the others the 4-wave one; both must meet the contract bound."""
-    say("gemm scale layout %s %dx%dx%d" % (layout, M, N, K))
+    kernel, the others the 4-wave one; both must meet their accumulation mode's bound."""
+    say("gemm scale layout %s %dx%dx%d accum %s" % (layout, M, N, K, accum))
     rng = np.random.default_rng(11)
     xc, xs = quantized(rng, M, K, 1.0, "e4m3")
     wc, ws = quantized(rng, N, K, 0.02, "e4m3")
@@ -120,11 +121,12 @@ def test_gemm_scale_layouts(M, N, K, layout):
           "ld odd": nb + 1 + (nb % 2), "unaligned": nb + 4}[layout]
     off = 1 if layout == "unaligned" else 0
     xs2, ws2 = strided_scales(xs, ld, off), strided_scales(ws, ld, off)
-    y = mxq.gemm(xc, xs2, wc, ws2, K, out_dtype=torch.float32)
-    y0 = mxq.gemm(xc, xs, wc, ws, K, out_dtype=torch.float32)
+    y = mxq.gemm(xc, xs2, wc, ws2, K, out_dtype=torch.float32, accum=accum)
+    y0 = mxq.gemm(xc, xs, wc, ws, K, out_dtype=torch.float32, accum=accum)
     torch.cuda.synchronize()
-    full_check(xc, xs, "e4m3", wc, ws, "e4m3", K, y, torch.float32, what="layout " + layout)
-    full_check(xc, xs, "e4m3", wc, ws, "e4m3", K, y0, torch.float32, what="padded scales")
+    strict = accum == "fp32"
+    full_check(xc, xs, "e4m3", wc, ws, "e4m3", K, y, torch.float32, what="layout " + layout, strict=strict)
+    full_check(xc, xs, "e4m3", wc, ws, "e4m3", K, y0, torch.float32, what="padded scales", strict=strict)
 
 
 @pytest.mark.parametrize("accum", ACCS)
