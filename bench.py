@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_MXFP8_TFLOPS = 5000.0      # MI355X dense FP8 / MXFP8 matrix-core peak
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix-core peak (the exact-product mode's MFMAs)
 PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -287,13 +288,14 @@ def main():
         "config": {"workload": "projection GEMM M=8192 K=4096 N=4096: bf16 X ~N(0,1) with 0.1% x100, "
                                "bf16 W ~N(0,0.02); quantize X and W rowwise to MXFP8 E4M3, GEMM with bf16 output",
                    "M": M, "K": K, "N": N, "step": "quantize(X) + quantize(W) + gemm"},
-        "roofline": {"bound": "mfma", "kernel": "mxq gemm (k_gemm)", "achieved": round(gemm_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "mxq gemm (pp::k_gemm_pp, fp8 matrix-core accumulation)", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_MXFP8_TFLOPS, 4),
                      "traffic": traffic, "algorithmic_bytes": int(gemm_bytes), "ms_avg": round(gemm_ms_avg, 5)},
         "components": {
             "gemm": {"ms": round(gemm_ms_avg, 5), "tflops": round(gemm_tflops, 2), "accum": "fp8 matrix cores"},
             "gemm_exact_accum": {"ms": round(exact_ms, 5), "tflops": round(exact_tflops, 2),
                                  "frac_of_fp8_peak": round(exact_tflops / PEAK_MXFP8_TFLOPS, 4),
+                                 "frac_of_bf16_peak": round(exact_tflops / PEAK_BF16_TFLOPS, 4),
                                  "accum": "exact products, fp32 sums (bf16 matrix cores)"},
             "quantize_x": {"ms": round(xq_ms, 5), "gbs": round(xq_gbs, 1), "bytes": int(M * K * 3.03125)},
             "quantize_2p28_e5m2": {"ms": round(e5_ms, 5), "gbs": round(q_bytes / (e5_ms * 1e-3) / 1e9, 1)},

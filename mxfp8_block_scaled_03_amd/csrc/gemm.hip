@@ -628,7 +628,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
 }
 
-template <int FA, int FB, bool EXACT>
+template <int FA, int FB, bool EXACT, bool TAIL>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, int tiles_m, int tiles_n,
                                                         const uint8_t* __restrict__ xc, int64_t ld_x,
                                                         const uint8_t* __restrict__ xs, int64_t ld_xs,
@@ -957,19 +957,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
   // steps 0..T-2 in pairs (even step: opsel byte 0, odd: byte 2); the last step, which
   // may be partial, on its own
   int s = 0;
-  for (; s + 2 <= T - 1; s += 2) {
-    any_step(s, C0(), No());
-    any_step(s + 1, C1(), No());
-  }
-  if (s < T - 1) {
-    any_step(s, C0(), No());
-    ++s;
-  }
-  if (T > 0) {
-    if (s & 1)
-      any_step(s, C1(), Yes());
-    else
-      any_step(s, C0(), Yes());
+  if constexpr (TAIL) {
+    for (; s + 2 <= T - 1; s += 2) {
+      any_step(s, C0(), No());
+      any_step(s + 1, C1(), No());
+    }
+    if (s < T - 1) {
+      any_step(s, C0(), No());
+      ++s;
+    }
+    if (T > 0) {
+      if (s & 1)
+        any_step(s, C1(), Yes());
+      else
+        any_step(s, C0(), Yes());
+    }
+  } else {
+    // K a multiple of 64: no step needs masking, so the last one runs as any other (its
+    // DMA of steps >= T reads empty ranges); the epilogue reuses the code stages, so every
+    // wave's loads must have landed before any wave writes there
+    for (; s + 2 <= T; s += 2) {
+      any_step(s, C0(), No());
+      any_step(s + 1, C1(), No());
+    }
+    if (s < T) any_step(s, C0(), No());
+    wait_vm<0>();
+    lds_barrier();
   }
   if (gp == 0) lds_barrier();   // matches group 1's extra barrier: all LDS reads are done
 
@@ -1117,12 +1130,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
   }
 }
 
-template <int FA, int FB, bool EXACT>
-hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
+template <int FA, int FB, bool EXACT, bool TAIL>
+hipError_t launch_t(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
                     int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
                     const GemmEpilogue& ep, hipStream_t stream) {
   static bool attr_set[64] = {false};
-  auto kern = k_gemm_pp<FA, FB, EXACT>;
+  auto kern = k_gemm_pp<FA, FB, EXACT, TAIL>;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (!attr_set[dev]) {
@@ -1134,6 +1147,15 @@ hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t 
   hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreads), kLdsBytes, stream, (int)M, (int)N, (int)K, tiles_m,
                      tiles_n, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep);
   return hipGetLastError();
+}
+
+// K not a multiple of 64: the kernel with the masked last step
+template <int FA, int FB, bool EXACT>
+hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
+                    int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
+                    const GemmEpilogue& ep, hipStream_t stream) {
+  if (K % 64 != 0) return launch_t<FA, FB, EXACT, true>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+  return launch_t<FA, FB, EXACT, false>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
 }
 
 template <bool EXACT>
