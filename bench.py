@@ -269,7 +269,78 @@ def main():
     up_unfused_ms = time_calls(unfused_pair)
     up_fused_ms = time_calls(lambda: L.mxq_gemm_ex(*up_fused))
     up_flops = 2.0 * T3 * I3 * H3
-    del f_xc, f_xs, f_wc, f_ws, f_b, y1, y1c, y1s
+
+    # ---- the other configurations' GEMMs, each timed in both accumulation modes (raw C
+    #      calls, 10 launches between two events).  FFN down consumes the fused up
+    #      projection's Y1 codes; backward dgrad/wgrad use E5M2 gradient codes; K=4000 runs
+    #      the kernel with a masked last K step; the 256x256x512 case is launch-bound.
+    def gemm_args(Mg, Ng, Kg, a, b, fa, fb, yt, ydt, bias=None):
+        (ac, as_), (bc, bs) = a, b
+        return [Mg, Ng, Kg, ac.data_ptr(), ac.stride(0), as_.data_ptr(), as_.stride(0), fa, bc.data_ptr(), bc.stride(0),
+                bs.data_ptr(), bs.stride(0), fb, ctypes.c_float(1.0), None if bias is None else bias.data_ptr(),
+                yt.data_ptr(), ydt, yt.stride(0), mxq.MXQ_ACC_FP8_MFMA, sh]
+
+    def time_gemm(name, ga, flops_g):
+        res = {"M": ga[0], "N": ga[1], "K": ga[2]}
+        for acc, key in ((mxq.MXQ_ACC_FP8_MFMA, ""), (mxq.MXQ_ACC_FP32, "exact_")):
+            ga[18] = acc
+            st = L.mxq_gemm(*ga)
+            if st != 0:
+                raise RuntimeError("%s gemm failed: %s" % (name, mxq.mxq_status_string(st)))
+            ms_g = time_calls(lambda: L.mxq_gemm(*ga))
+            res[key + "ms"] = round(ms_g, 5)
+            res[key + "tflops"] = round(flops_g / (ms_g * 1e-3) / 1e12, 2)
+        res["frac_of_fp8_peak"] = round(res["tflops"] / PEAK_MXFP8_TFLOPS, 4)
+        res["exact_frac_of_bf16_peak"] = round(res["exact_tflops"] / PEAK_BF16_TFLOPS, 4)
+        return res
+
+    configs = {}
+    d3 = wl.workload3()
+    w2q = mxq.quantize(d3["w2"].to(dev), "e4m3", "row")
+    b2 = d3["b2"].to(dev)
+    del d3
+    y2 = torch.empty((T3, H3), dtype=torch.bfloat16, device=dev)
+    configs["ffn_down_16384x5120x8192_bias_bf16"] = time_gemm(
+        "ffn down", gemm_args(T3, H3, I3, (y1c, y1s), w2q, mxq.MXQ_E4M3, mxq.MXQ_E4M3, y2, mxq.MXQ_BF16, b2),
+        2.0 * T3 * H3 * I3)
+    del f_xc, f_xs, f_wc, f_ws, f_b, y1, y1c, y1s, w2q, b2, y2
+
+    d4 = wl.workload4()
+    M4, K4, N4 = d4["M"], d4["K"], d4["N"]
+    dy_row = mxq.quantize(d4["dy"].to(dev), "e5m2", "row")       # [M][N] along N
+    w_col = mxq.quantize(d4["w"].to(dev), "e4m3", "col")         # W [N][K] -> [K][N] along N
+    dx = torch.empty((M4, K4), dtype=torch.float32, device=dev)
+    configs["dgrad_8192x4096x4096_e5m2xe4m3_fp32"] = time_gemm(
+        "dgrad", gemm_args(M4, K4, N4, dy_row, w_col, mxq.MXQ_E5M2, mxq.MXQ_E4M3, dx, mxq.MXQ_F32),
+        2.0 * M4 * K4 * N4)
+    del dy_row, w_col, dx
+    dy_col = mxq.quantize(d4["dy"].to(dev), "e5m2", "col")       # [N][M] along M
+    x_col = mxq.quantize(d4["x"].to(dev), "e4m3", "col")         # [K][M] along M
+    dw = torch.empty((N4, K4), dtype=torch.float32, device=dev)
+    configs["wgrad_4096x4096x8192_e5m2xe4m3_fp32"] = time_gemm(
+        "wgrad", gemm_args(N4, K4, M4, dy_col, x_col, mxq.MXQ_E5M2, mxq.MXQ_E4M3, dw, mxq.MXQ_F32),
+        2.0 * N4 * K4 * M4)
+    del d4, dy_col, x_col, dw
+
+    d5 = wl.workload5()
+    M5, K5, N5 = d5["M"], d5["K"], d5["N"]
+    x5 = mxq.quantize(d5["x"].to(dev), "e4m3", "row")
+    w5 = mxq.quantize(d5["w"].to(dev), "e4m3", "row")
+    del d5
+    y5 = torch.empty((M5, N5), dtype=torch.float32, device=dev)
+    configs["ragged_4096x6144x4000_fp32"] = time_gemm(
+        "ragged", gemm_args(M5, N5, K5, x5, w5, mxq.MXQ_E4M3, mxq.MXQ_E4M3, y5, mxq.MXQ_F32), 2.0 * M5 * N5 * K5)
+    del x5, w5, y5
+
+    d1 = wl.workload1()
+    M1, K1, N1 = d1["M"], d1["K"], d1["N"]
+    x1 = mxq.quantize(d1["x"].to(dev), "e4m3", "row")
+    w1 = mxq.quantize(d1["w_kn"].to(dev), "e4m3", "col")
+    del d1
+    y1f = torch.empty((M1, N1), dtype=torch.float32, device=dev)
+    configs["small_256x256x512_fp32_launch_bound"] = time_gemm(
+        "small", gemm_args(M1, N1, K1, x1, w1, mxq.MXQ_E4M3, mxq.MXQ_E4M3, y1f, mxq.MXQ_F32), 2.0 * M1 * N1 * K1)
+    del x1, w1, y1f
 
     traffic = load_traffic("gemm")
     out = {
@@ -312,6 +383,7 @@ def main():
                                   "tflops": round(up_flops / (up_fused_ms * 1e-3) / 1e12, 2),
                                   "speedup_vs_unfused": round(up_unfused_ms / up_fused_ms, 3),
                                   "what": "same GEMM writing Y1's MX codes and scales from its epilogue"},
+            "configs": configs,
             "quantize_2p28": {"ms": round(q_ms, 5), "gbs": round(q_gbs, 1), "frac_hbm": round(q_gbs / PEAK_HBM_GBS, 4),
                               "bytes": int(q_bytes), "workload": "[16384][16384] bf16 Laplace(0,1) 1% x1e4, rowwise E4M3"},
         },

@@ -835,7 +835,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
       for (int f = 0; f < 2; ++f) sb[f] = *reinterpret_cast<const uint32_t*>(smem + rsb + ss + 512 * f);
     }
     bool dead_block = false;
-    if (decltype(last)::value) {
+    if (decltype(last)::value || (TAIL && s == T - 1)) {
       if ((K & 63) != 0) {
         // dword e of this half holds k = 64s + 32h + 16g + 4e .. +3
 #pragma unroll
@@ -957,7 +957,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
   // steps 0..T-2 in pairs (even step: opsel byte 0, odd: byte 2); the last step, which
   // may be partial, on its own
   int s = 0;
-  if constexpr (TAIL) {
+  if constexpr (TAIL && !EXACT) {
+    // matrix-core mode, K not a multiple of 64: the last step is peeled (masked code bytes
+    // at k >= K, blocks >= nb replaced), which keeps the masking out of the loop's registers
     for (; s + 2 <= T - 1; s += 2) {
       any_step(s, C0(), No());
       any_step(s + 1, C1(), No());
@@ -973,9 +975,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
         any_step(s, C0(), Yes());
     }
   } else {
-    // K a multiple of 64: no step needs masking, so the last one runs as any other (its
-    // DMA of steps >= T reads empty ranges); the epilogue reuses the code stages, so every
-    // wave's loads must have landed before any wave writes there
+    // every step runs through the same loop: the last one's DMA of steps >= T reads empty
+    // ranges, and in the exact mode with K not a multiple of 64 its memory phase masks code
+    // bytes at k >= K and blocks >= nb behind a uniform branch.  The epilogue reuses the
+    // code stages, so every wave's loads must have landed before any wave writes there.
     for (; s + 2 <= T; s += 2) {
       any_step(s, C0(), No());
       any_step(s + 1, C1(), No());
