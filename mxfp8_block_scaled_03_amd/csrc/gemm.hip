@@ -16,6 +16,7 @@
 // taken from byte 0 or 2 of the register by opsel.  Output: lane l, register r holds
 // D[8*(r/4) + 4*g + r%4][i].
 //
+// Fallback kernel (scale rows that are not 16-byte aligned, both accumulation modes).
 // Tiling: 256x256 output tile per workgroup of 4 waves (2x2 waves of 128x128), K step of
 // 128 bytes.  Code tiles move global -> LDS with buffer_load ... lds (16 bytes per lane,
 // no VGPR staging), double-buffered, with a 16-byte-chunk XOR swizzle so the fragment
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(int M, int N, int K, int t
 }
 
 // ---------------------------------------------------------------------------------------
-// Ping-pong kernel for the matrix-core accumulation mode.
+// Ping-pong kernel (both accumulation modes; 16-byte aligned scale rows).
 //
 // 8 waves, 256x256 output tile, 64-byte K steps, 4 LDS code stages.  Waves w and w+4
 // share a SIMD; waves 0-3 (group 0) own output rows 0-127 of the tile and waves 4-7
@@ -498,6 +499,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(int M, int N, int K, int t
 // a lane ends up holding four consecutive output columns of one row; interior tiles are
 // written through LDS as 16-byte row segments.  Requires 16-byte aligned scale rows
 // (scale base and leading dimension).
+//
+// The exact-product mode (EXACT) splits each step into two half steps, one per 32-K block,
+// decodes the codes to bf16 with their block scale in its memory phases and runs bf16 MFMAs
+// in its compute phases (see memory_half / compute_half).  With K a multiple of 64 (!TAIL)
+// every step runs through one loop; otherwise the matrix-core mode peels the last, masked
+// step and the exact mode masks it inside the loop.
 namespace pp {
 
 constexpr int kThreads = 512;
