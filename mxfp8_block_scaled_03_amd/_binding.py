@@ -97,14 +97,14 @@ def mxq_dequantize(codes, ld_codes, scales, ld_scales, elem, L, K, dst, dst_type
 
 
 def mxq_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws, w_elem,
-             alpha, bias, y, y_type, ld_y, accum=MXQ_ACC_FP8_MFMA, stream=None) -> int:
+             alpha, bias, y, y_type, ld_y, accum=MXQ_ACC_FP32, stream=None) -> int:
     return lib().mxq_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws,
                           w_elem, alpha, bias, y, y_type, ld_y, accum, stream)
 
 
 def mxq_gemm_ex(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws, w_elem,
                 alpha, bias, act, y, y_type, ld_y, q_elem, q_codes, ld_q_codes, q_scales, ld_q_scales,
-                accum=MXQ_ACC_FP8_MFMA, stream=None) -> int:
+                accum=MXQ_ACC_FP32, stream=None) -> int:
     return lib().mxq_gemm_ex(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws,
                              w_elem, alpha, bias, act, y, y_type, ld_y, q_elem, q_codes, ld_q_codes, q_scales,
                              ld_q_scales, accum, stream)
@@ -148,6 +148,48 @@ def _round_up(v: int, m: int) -> int:
     return (v + m - 1) // m * m
 
 
+# Argument checks of the torch conveniences.  The C ABI sees only pointers, so an
+# undersized or host-resident tensor would reach a kernel as an out-of-bounds or host
+# address; these checks run first and raise ValueError.  Dtype and shape are checked
+# before the device, so every rejection can be exercised without a GPU.
+
+def _req_2d(t, name: str, dtype=None, min_rows=None, min_cols=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D, got shape %s" % (name, tuple(t.shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.shape[0] > 1 and t.shape[1] > 0 and t.stride(1) != 1:
+        raise ValueError("%s must have unit stride along its last dimension" % name)
+    if t.shape[0] > 1 and t.stride(0) < t.shape[1]:
+        raise ValueError("%s rows overlap (row stride %d < %d columns)" % (name, t.stride(0), t.shape[1]))
+    if min_rows is not None and t.shape[0] < min_rows:
+        raise ValueError("%s has %d rows, needs at least %d" % (name, t.shape[0], min_rows))
+    if min_cols is not None and t.shape[1] < min_cols:
+        raise ValueError("%s has %d columns, needs at least %d" % (name, t.shape[1], min_cols))
+
+
+def _req_cuda(*named):
+    for name, t in named:
+        if t is not None and not t.is_cuda:
+            raise ValueError("%s must be a CUDA (HIP device) tensor, got device %s" % (name, t.device))
+
+
+def _req_wide(t, name: str):
+    torch = _torch()
+    _req_2d(t, name)
+    if t.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("%s must be float32 or bfloat16, got %s" % (name, t.dtype))
+
+
+def _ld(t) -> int:
+    """Leading dimension passed to the ABI: the row stride, or the width where the stride
+    says nothing about the layout (no rows, or a single row of a broadcast view)."""
+    return t.stride(0) if t.shape[0] > 0 and t.stride(0) >= t.shape[1] else max(t.shape[1], 1)
+
+
 def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None):
     """MX-quantize a 2-D bf16/fp32 CUDA tensor.
 
@@ -160,21 +202,25 @@ def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None):
     the layout the fastest GEMM kernel reads.
     """
     torch = _torch()
-    if x.dim() != 2:
-        raise ValueError("quantize expects a 2-D tensor")
-    if x.stride(1) != 1:
-        raise ValueError("quantize expects unit stride along the last dimension")
+    _req_wide(x, "x")
+    if axis not in _AXIS or elem not in _ELEM:
+        raise ValueError("axis must be 'row' or 'col' and elem 'e4m3' or 'e5m2'")
     rows, cols = x.shape
     ax = _AXIS[axis]
     L, K = (rows, cols) if ax == MXQ_ROWWISE else (cols, rows)
     Kp = _round_up(K, 32)
+    nb = Kp // 32
+    if codes is not None:
+        _req_2d(codes, "codes", torch.uint8, L, Kp)
+    if scales is not None:
+        _req_2d(scales, "scales", torch.uint8, L, nb)
+    _req_cuda(("x", x), ("codes", codes), ("scales", scales))
     if codes is None:
         codes = torch.empty((L, Kp), dtype=torch.uint8, device=x.device)
     if scales is None:
-        nb = Kp // 32
         scales = torch.empty((L, _round_up(nb, 16)), dtype=torch.uint8, device=x.device)[:, :nb]
-    st = mxq_quantize(x.data_ptr(), _wide_type(x), rows, cols, x.stride(0) if rows > 0 else cols, ax,
-                      _ELEM[elem], codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0),
+    st = mxq_quantize(x.data_ptr(), _wide_type(x), rows, cols, _ld(x), ax,
+                      _ELEM[elem], codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales),
                       _stream_handle())
     _check(st, "mxq_quantize")
     return codes, scales
@@ -184,18 +230,24 @@ def quantize_sr(x, seed: int, elem: str = "e5m2", axis: str = "row", codes=None,
     """quantize() with stochastically rounded codes (Philox4x32-10 keyed by `seed`, see
     mxq_quantize_sr); E5M2 by default, the gradient format."""
     torch = _torch()
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("quantize_sr expects a 2-D tensor with unit stride along the last dimension")
+    _req_wide(x, "x")
+    if axis not in ("row", "col") or elem not in _ELEM:
+        raise ValueError("axis must be 'row' or 'col' and elem 'e4m3' or 'e5m2'")
     rows, cols = x.shape
     L, K = (rows, cols) if axis == "row" else (cols, rows)
     Kp = _round_up(K, 32)
+    if codes is not None:
+        _req_2d(codes, "codes", torch.uint8, L, Kp)
+    if scales is not None:
+        _req_2d(scales, "scales", torch.uint8, L, Kp // 32)
+    _req_cuda(("x", x), ("codes", codes), ("scales", scales))
     if codes is None:
         codes = torch.empty((L, Kp), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((L, _round_up(Kp // 32, 16)), dtype=torch.uint8, device=x.device)[:, :Kp // 32]
-    st = mxq_quantize_sr(x.data_ptr(), _wide_type(x), rows, cols, x.stride(0) if rows > 0 else cols,
+    st = mxq_quantize_sr(x.data_ptr(), _wide_type(x), rows, cols, _ld(x),
                          MXQ_ROWWISE if axis == "row" else MXQ_COLWISE, _ELEM[elem], int(seed) & (2 ** 64 - 1),
-                         codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0), _stream_handle())
+                         codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales), _stream_handle())
     _check(st, "mxq_quantize_sr")
     return codes, scales
 
@@ -206,21 +258,24 @@ def quantize_scaled(x, scales, elem: str = "e4m3", axis: str = "row", diagnostic
     Returns codes [L][Kp], or (codes, amax [L][nb] float32, clipped [L][nb] uint8,
     flushed [L][nb] uint8) with diagnostics=True (see mxq_quantize_scaled)."""
     torch = _torch()
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("quantize_scaled expects a 2-D tensor with unit stride along the last dimension")
+    _req_wide(x, "x")
+    if axis not in ("row", "col") or elem not in _ELEM:
+        raise ValueError("axis must be 'row' or 'col' and elem 'e4m3' or 'e5m2'")
     rows, cols = x.shape
     L, K = (rows, cols) if axis == "row" else (cols, rows)
     Kp = _round_up(K, 32)
     nb = Kp // 32
-    if scales.dtype != torch.uint8 or tuple(scales.shape) != (L, nb) or (L > 0 and scales.stride(1) != 1):
-        raise ValueError("scales must be a uint8 [L][nb] tensor with unit inner stride")
+    _req_2d(scales, "scales", torch.uint8)
+    if tuple(scales.shape) != (L, nb):
+        raise ValueError("scales must be a uint8 [L][nb] = [%d][%d] tensor, got %s" % (L, nb, tuple(scales.shape)))
+    _req_cuda(("x", x), ("scales", scales))
     codes = torch.empty((L, Kp), dtype=torch.uint8, device=x.device)
     amax = clipped = flushed = None
     if diagnostics:
         amax = torch.empty((L, nb), dtype=torch.float32, device=x.device)
         clipped = torch.empty((L, nb), dtype=torch.uint8, device=x.device)
         flushed = torch.empty((L, nb), dtype=torch.uint8, device=x.device)
-    st = mxq_quantize_scaled(x.data_ptr(), _wide_type(x), rows, cols, x.stride(0) if rows > 0 else cols,
+    st = mxq_quantize_scaled(x.data_ptr(), _wide_type(x), rows, cols, _ld(x),
                              MXQ_ROWWISE if axis == "row" else MXQ_COLWISE, _ELEM[elem], scales.data_ptr(),
                              scales.stride(0) if L > 0 else nb, codes.data_ptr(), codes.stride(0),
                              None if amax is None else amax.data_ptr(), nb,
@@ -238,17 +293,17 @@ def quantize_dual(x, elem: str = "e4m3"):
     quantize(x, elem, "row") and quantize(x, elem, "col").
     """
     torch = _torch()
-    if x.dim() != 2:
-        raise ValueError("quantize_dual expects a 2-D tensor")
-    if x.stride(1) != 1:
-        raise ValueError("quantize_dual expects unit stride along the last dimension")
+    _req_wide(x, "x")
+    if elem not in _ELEM:
+        raise ValueError("elem must be 'e4m3' or 'e5m2'")
+    _req_cuda(("x", x))
     rows, cols = x.shape
     kp_r, kp_c = _round_up(cols, 32), _round_up(rows, 32)
     rc = torch.empty((rows, kp_r), dtype=torch.uint8, device=x.device)
     rs = torch.empty((rows, _round_up(kp_r // 32, 16)), dtype=torch.uint8, device=x.device)[:, :kp_r // 32]
     cc = torch.empty((cols, kp_c), dtype=torch.uint8, device=x.device)
     cs = torch.empty((cols, _round_up(kp_c // 32, 16)), dtype=torch.uint8, device=x.device)[:, :kp_c // 32]
-    st = mxq_quantize_dual(x.data_ptr(), _wide_type(x), rows, cols, x.stride(0) if rows > 0 else cols, _ELEM[elem],
+    st = mxq_quantize_dual(x.data_ptr(), _wide_type(x), rows, cols, _ld(x), _ELEM[elem],
                            rc.data_ptr(), rc.stride(0), rs.data_ptr(), rs.stride(0), cc.data_ptr(), cc.stride(0),
                            cs.data_ptr(), cs.stride(0), _stream_handle())
     _check(st, "mxq_quantize_dual")
@@ -259,32 +314,61 @@ def dequantize(codes, scales, K: int, elem: str = "e4m3", out_dtype=None):
     """Reconstruct dec(code) * 2^(s-127) as fp32 (default) or bf16, shape [L][K]."""
     torch = _torch()
     out_dtype = out_dtype or torch.float32
+    if out_dtype not in (torch.float32, torch.bfloat16) or elem not in _ELEM:
+        raise ValueError("out_dtype must be float32 or bfloat16 and elem 'e4m3' or 'e5m2'")
+    if K < 0:
+        raise ValueError("K must be >= 0")
+    _req_2d(codes, "codes", torch.uint8, None, K)
     L = codes.shape[0]
+    _req_2d(scales, "scales", torch.uint8, L, (K + 31) // 32)
+    _req_cuda(("codes", codes), ("scales", scales))
     dst = torch.empty((L, K), dtype=out_dtype, device=codes.device)
-    st = mxq_dequantize(codes.data_ptr(), codes.stride(0), scales.data_ptr(), scales.stride(0), _ELEM[elem], L, K,
-                        dst.data_ptr(), _wide_type(dst), K, _stream_handle())
+    st = mxq_dequantize(codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales), _ELEM[elem], L, K,
+                        dst.data_ptr(), _wide_type(dst), max(K, 1), _stream_handle())
     _check(st, "mxq_dequantize")
     return dst
 
 
 def gemm(x_codes, x_scales, w_codes, w_scales, K: int, x_elem: str = "e4m3", w_elem: str = "e4m3",
-         alpha: float = 1.0, bias=None, out_dtype=None, out=None, accum: str = "fp8", act=None,
+         alpha: float = 1.0, bias=None, out_dtype=None, out=None, accum: str = "fp32", act=None,
          quant_out=None, wide_out: bool = True):
     """Y[M][N] = act(alpha * (X W) + bias) with X = (x_codes [M][Kp], x_scales) and W column-major
-    (w_codes [N][Kp], w_scales).  accum="fp8": FP8 matrix cores (fast); accum="fp32":
-    exact products summed in FP32 (see mxq_accum in include/mxq.h).  act: None or "silu".
+    (w_codes [N][Kp], w_scales).  accum="fp32" (default): exact products summed in FP32, the
+    mode that meets |Y - Y_ref| <= 1e-5 * sum_k |s x w|; accum="fp8": the FP8 matrix cores,
+    faster, but each group of 8 products is truncated ~13 bits below its largest, outside
+    that bound (see mxq_accum in include/mxq.h).  act: None or "silu".
 
     quant_out="e4m3"/"e5m2" also returns the MX codes [M][Np] and scales of bf16(Y) along
     N, produced in the GEMM's epilogue (byte for byte quantize(Y_bf16, elem, "row"));
     wide_out=False then skips writing Y.  Returns Y, or (Y or None, codes, scales)."""
     torch = _torch()
+    if K < 0:
+        raise ValueError("K must be >= 0")
+    Kp = _round_up(K, 32)
+    nb = Kp // 32
+    _req_2d(x_codes, "x_codes", torch.uint8, None, Kp)
+    _req_2d(w_codes, "w_codes", torch.uint8, None, Kp)
     M, N = x_codes.shape[0], w_codes.shape[0]
-    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != N):
-        raise ValueError("bias must be a float32 tensor of N elements")
+    _req_2d(x_scales, "x_scales", torch.uint8, M, nb)
+    _req_2d(w_scales, "w_scales", torch.uint8, N, nb)
+    if x_elem not in _ELEM or w_elem not in _ELEM or (quant_out is not None and quant_out not in _ELEM):
+        raise ValueError("element formats must be 'e4m3' or 'e5m2'")
+    if accum not in _ACC:
+        raise ValueError("accum must be 'fp32' or 'fp8'")
+    if bias is not None:
+        if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or bias.numel() != N \
+                or (N > 1 and bias.stride(-1) != 1) or bias.dim() != 1:
+            raise ValueError("bias must be a contiguous 1-D float32 tensor of N = %d elements" % N)
     if act not in _ACT:
         raise ValueError("act must be None or 'silu'")
     if quant_out is None and not wide_out:
         raise ValueError("nothing to write: wide_out=False needs quant_out")
+    if wide_out and out is not None:
+        _req_wide(out, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out must have shape (M, N) = (%d, %d), got %s" % (M, N, tuple(out.shape)))
+    _req_cuda(("x_codes", x_codes), ("x_scales", x_scales), ("w_codes", w_codes), ("w_scales", w_scales),
+              ("bias", bias), ("out", out if wide_out else None))
     if wide_out and out is None:
         out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=x_codes.device)
     y = out if wide_out else None
@@ -293,13 +377,13 @@ def gemm(x_codes, x_scales, w_codes, w_scales, K: int, x_elem: str = "e4m3", w_e
         np_ = _round_up(N, 32)
         qc = torch.empty((M, np_), dtype=torch.uint8, device=x_codes.device)
         qs = torch.empty((M, _round_up(np_ // 32, 16)), dtype=torch.uint8, device=x_codes.device)[:, :np_ // 32]
-    st = mxq_gemm_ex(M, N, K, x_codes.data_ptr(), x_codes.stride(0), x_scales.data_ptr(), x_scales.stride(0),
-                     _ELEM[x_elem], w_codes.data_ptr(), w_codes.stride(0), w_scales.data_ptr(), w_scales.stride(0),
+    st = mxq_gemm_ex(M, N, K, x_codes.data_ptr(), _ld(x_codes), x_scales.data_ptr(), _ld(x_scales),
+                     _ELEM[x_elem], w_codes.data_ptr(), _ld(w_codes), w_scales.data_ptr(), _ld(w_scales),
                      _ELEM[w_elem], float(alpha), None if bias is None else bias.data_ptr(), _ACT[act],
                      None if y is None else y.data_ptr(), MXQ_BF16 if y is None else _wide_type(y),
-                     0 if y is None else y.stride(0), _ELEM[quant_out or "e4m3"],
-                     None if qc is None else qc.data_ptr(), 0 if qc is None else qc.stride(0),
-                     None if qs is None else qs.data_ptr(), 0 if qs is None else qs.stride(0),
+                     0 if y is None else _ld(y), _ELEM[quant_out or "e4m3"],
+                     None if qc is None else qc.data_ptr(), 0 if qc is None else _ld(qc),
+                     None if qs is None else qs.data_ptr(), 0 if qs is None else _ld(qs),
                      _ACC[accum], _stream_handle())
     _check(st, "mxq_gemm_ex")
     if quant_out is None:

@@ -20,8 +20,12 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libmxo.so")
 _SRC = os.path.join(_HERE, "mxo.c")
+# MXO_SANITIZE=1 selects a build of mxo.c instrumented with AddressSanitizer and
+# UndefinedBehaviorSanitizer (libmxo_san.so; the interpreter must then run with libasan
+# preloaded, e.g. LD_PRELOAD=$(gcc -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0).
+_SANITIZE = os.environ.get("MXO_SANITIZE", "") == "1"
+_LIB_PATH = os.path.join(_HERE, "libmxo_san.so" if _SANITIZE else "libmxo.so")
 
 FMT = {"e4m3": 0, "e5m2": 1}
 SRC = {"f32": 0, "bf16": 1}
@@ -31,8 +35,10 @@ def build(force: bool = True) -> str:
     """Compile mxo.c into libmxo.so with gcc (-O2, OpenMP, strict IEEE: no fast-math)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        san = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+               "-fno-sanitize-recover=undefined"] if _SANITIZE else []
         subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
-                               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"])
+                               "-fno-fast-math", "-ffp-contract=off"] + san + [_SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 

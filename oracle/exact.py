@@ -32,13 +32,17 @@ FORMATS = {
 }
 
 
-def decode_e8m0(code):
-    """2^(code-127) for code 0..254, NaN for 255; ValueError for anything else."""
-    if type(code) is not int or not 0 <= code <= 255:
-        raise ValueError("an unsigned scale byte is required")
-    if code == 255:
-        return math.nan
-    return Fraction(2) ** (code - 127)
+_E8M0_NAN = 0xFF          # the one non-numeric E8M0 byte
+
+
+def decode_e8m0(byte):
+    """Value of an E8M0 scale byte: an 8-bit biased exponent with no sign and no mantissa,
+    bias 127, so byte c stands for 2^(c - 127) exactly (a Fraction); 0xFF is NaN.
+    Arguments that are not a Python int in 0..255 are not scale bytes (ValueError)."""
+    is_byte = isinstance(byte, int) and not isinstance(byte, bool) and (byte & ~0xFF) == 0
+    if not is_byte:
+        raise ValueError("E8M0 scale bytes are integers 0..255, got %r" % (byte,))
+    return math.nan if byte == _E8M0_NAN else Fraction(1, 1 << 127) * (1 << byte)
 
 
 def e8m0_exact(code: int) -> Fraction:

@@ -20,15 +20,18 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 def test_traffic_is_keyed_to_the_gemm_source(tmp_path, monkeypatch):
     with open(bench.TRAFFIC_FILE) as f:
-        rec = json.load(f)["gemm"]
-    # the record's parts add up; it is reported exactly when it was taken on this source
-    assert rec["bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
-    current = rec["source_sha256"] == bench.source_digest(bench.GEMM_SOURCE)
-    assert bench.load_traffic("gemm") == (rec["bytes_per_launch"] if current else None)
+        recs = json.load(f)
+    assert recs
+    for key, rec in recs.items():
+        # the record's parts add up; it is reported exactly when it was taken on this source
+        assert rec["bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+        current = rec["source_sha256"] == bench.source_digest(bench.GEMM_SOURCE)
+        assert bench.load_traffic(key) == (rec["bytes_per_launch"] if current else None)
     # a changed source (or a missing record) reports no traffic
     src = tmp_path / "gemm.hip"
     src.write_bytes(open(bench.GEMM_SOURCE, "rb").read() + b"\n")
     monkeypatch.setattr(bench, "GEMM_SOURCE", str(src))
-    assert bench.load_traffic("gemm") is None
+    for key in recs:
+        assert bench.load_traffic(key) is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
-    assert bench.load_traffic("gemm") is None
+    assert bench.load_traffic("gemm_exact") is None

@@ -125,14 +125,67 @@ def test_fused_quant_respects_pitches_and_padding():
     c, s = qc.cpu().numpy(), qs.cpu().numpy()
     assert np.all(c[:, 128:] == 0xCD) and np.all(s[:, 4:] == 0xCD)
     assert np.all(c[:, 100:128] == 0)
-    y = mxq.gemm(xc, xs, wc, ws, K, bias=b, out_dtype=torch.bfloat16, act="silu")
+    y = mxq.gemm(xc, xs, wc, ws, K, bias=b, out_dtype=torch.bfloat16, act="silu", accum="fp8")
     oc, os_ = oracle.quantize(host_src(y.cpu()), "e5m2", axis=0)
     assert np.array_equal(c[:, :128], oc) and np.array_equal(s[:, :4], os_)
 
 
+def test_ffn_pair_full_size_exact_accumulation():
+    """The FFN pair T=16384, H=5120, I=8192 in the exact-product mode, at the strict bound
+    |y - y_ref| <= 1e-5 * T (+ the epilogue roundings) on sampled outputs:
+      - up projection with bias, FP32 and bf16 output;
+      - up projection with bias and SiLU against silu(y_ref) of the FP64 oracle (the strict
+        bound carried through SiLU, whose slope is at most 1.0998, plus the SiLU rounding);
+      - the producer-fused MX codes of bf16(silu(...)) equal the GPU quantize of the unfused
+        bf16 output everywhere and the oracle's quantize on sampled rows;
+      - the down projection on the fused codes, bf16 and FP32 output."""
+    d = wl.workload3()
+    T, H, I = d["T"], d["H"], d["I"]
+    say("ffn pair exact: quantize operands")
+    xc, xs = mxq.quantize(d["x"].to(DEV), "e4m3", "row")
+    w1c, w1s = mxq.quantize(d["w1"].to(DEV), "e4m3", "row")
+    w2c, w2s = mxq.quantize(d["w2"].to(DEV), "e4m3", "row")
+    b1, b2 = d["b1"].to(DEV), d["b2"].to(DEV)
+    del d
+    for out in (torch.float32, torch.bfloat16):
+        say("ffn pair exact: up projection, bias, %s out" % out)
+        v = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, out_dtype=out, accum="fp32")
+        sampled_check(xc, xs, "e4m3", w1c, w1s, "e4m3", H, v, out, bias=b1, what="up exact %s" % out, n=2000,
+                      strict=True)
+        del v
+    say("ffn pair exact: up projection with SiLU against the oracle")
+    s32 = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, out_dtype=torch.float32, act="silu", accum="fp32")
+    rng = np.random.default_rng(11)
+    ii, jj = rng.integers(0, T, 2000), rng.integers(0, I, 2000)
+    y_ref, t = oracle.gemm_sampled(xc.cpu().numpy(), xs.cpu().numpy(), "e4m3", w1c.cpu().numpy(), w1s.cpu().numpy(),
+                                   "e4m3", H, ii, jj, bias=b1.cpu().numpy())
+    ref = oracle.silu(y_ref)
+    got = s32.cpu().numpy()[ii, jj].astype(np.float64)
+    lim = 1.1 * (STRICT_REL * t + 2.0 ** -23 * np.abs(y_ref)) + SILU_REL * np.abs(ref) + SILU_ABS
+    assert np.all(np.abs(got - ref) <= lim), "silu(up) worst excess %g" % float(np.max(np.abs(got - ref) - lim))
+    del s32
+    say("ffn pair exact: fused MX output of the up projection")
+    y1 = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, out_dtype=torch.bfloat16, act="silu", accum="fp32")
+    _, qc, qs = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, act="silu", quant_out="e4m3", wide_out=False, accum="fp32")
+    gc, gs = mxq.quantize(y1, "e4m3", "row")
+    torch.cuda.synchronize()
+    assert torch.equal(qc, gc) and torch.equal(qs, gs), "fused codes differ from quantize(Y1)"
+    rows = np.random.default_rng(8).choice(T, 256, replace=False)
+    oc, os_ = oracle.quantize(host_src(y1[rows].cpu()), "e4m3", axis=0)
+    assert np.array_equal(qc[rows].cpu().numpy(), oc) and np.array_equal(qs[rows].cpu().numpy(), os_)
+    del y1, gc, gs
+    for out in (torch.bfloat16, torch.float32):
+        say("ffn pair exact: down projection on the fused codes, %s out" % out)
+        y2 = mxq.gemm(qc, qs, w2c, w2s, I, bias=b2, out_dtype=out, accum="fp32")
+        sampled_check(qc, qs, "e4m3", w2c, w2s, "e4m3", I, y2, out, bias=b2, what="down exact %s" % out, n=2000,
+                      strict=True)
+        del y2
+
+
 def test_ffn_pair_full_size_with_fused_quant():
-    """The FFN pair T=16384, H=5120, I=8192: the up projection with bias and SiLU writes the
-    MX codes of its output directly, and the down projection consumes them.  Checks: up
+    """The FFN pair T=16384, H=5120, I=8192 on the FP8 matrix cores (accum="fp8"): the up
+    projection with bias and SiLU writes the MX codes of its output directly, and the down
+    projection consumes them.  Checks: up
     projection (no activation) sampled against the oracle under the matrix-core bound; the
     SiLU output against the FP64 SiLU of the GPU's own pre-activation on sampled rows; the
     fused codes equal the GPU quantize of the unfused bf16 output everywhere and the
@@ -147,12 +200,12 @@ def test_ffn_pair_full_size_with_fused_quant():
     b1, b2 = d["b1"].to(DEV), d["b2"].to(DEV)
     del d
     say("ffn pair: up projection, pre-activation")
-    v = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, out_dtype=torch.float32)
+    v = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, out_dtype=torch.float32, accum="fp8")
     sampled_check(xc, xs, "e4m3", w1c, w1s, "e4m3", H, v, torch.float32, bias=b1, what="up", n=2000)
     say("ffn pair: up projection with SiLU, unfused and fused")
-    y1 = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, out_dtype=torch.bfloat16, act="silu")
-    s32 = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, out_dtype=torch.float32, act="silu")
-    _, qc, qs = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, act="silu", quant_out="e4m3", wide_out=False)
+    y1 = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, out_dtype=torch.bfloat16, act="silu", accum="fp8")
+    s32 = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, out_dtype=torch.float32, act="silu", accum="fp8")
+    _, qc, qs = mxq.gemm(xc, xs, w1c, w1s, H, bias=b1, act="silu", quant_out="e4m3", wide_out=False, accum="fp8")
     gc, gs = mxq.quantize(y1, "e4m3", "row")
     torch.cuda.synchronize()
     assert torch.equal(qc, gc) and torch.equal(qs, gs), "fused codes differ from quantize(Y1)"
@@ -165,5 +218,5 @@ def test_ffn_pair_full_size_with_fused_quant():
     assert np.array_equal(qc[rows].cpu().numpy(), oc) and np.array_equal(qs[rows].cpu().numpy(), os_)
     del v, s32, y1, gc, gs
     say("ffn pair: down projection on the fused codes")
-    y2 = mxq.gemm(qc, qs, w2c, w2s, I, bias=b2, out_dtype=torch.bfloat16)
+    y2 = mxq.gemm(qc, qs, w2c, w2s, I, bias=b2, out_dtype=torch.bfloat16, accum="fp8")
     sampled_check(qc, qs, "e4m3", w2c, w2s, "e4m3", I, y2, torch.bfloat16, bias=b2, what="down", n=2000)

@@ -159,7 +159,7 @@ def test_e8m0_pins(oracle_lib):
     assert oracle.decode_e8m0(0x80) == 2.0 == exact.decode_e8m0(0x80)
     assert oracle.decode_e8m0(0) > 0 and exact.decode_e8m0(0) > 0
     assert math.isnan(oracle.decode_e8m0(255)) and math.isnan(exact.decode_e8m0(255))
-    for bad in (-1, 256, 1.0, "x"):
+    for bad in (-1, 256, 1.0, "x", True, None):
         with pytest.raises(ValueError):
             exact.decode_e8m0(bad)
     assert [hex(c) for c in (-8 + 127, 1 + 127)] == g["printed_scale_bytes"]
