@@ -57,7 +57,7 @@ def parse():
 
 
 GEMM_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_03_amd", "csrc", "gemm.hip")
-GEMM_KERNEL_NAME = "mxq gemm, exact-product mode (pp::k_gemm_pp<0,0,true,false>: bf16 matrix cores)"
+GEMM_KERNEL_NAME = "mxq gemm, exact-product mode (ex::k_gemm_ex<0,0>: codes decoded to bf16 in registers, bf16 matrix cores)"
 FP8_LABEL = "FP8 matrix cores, 8-product groups truncated ~13 bits below their largest (outside 1e-5*T)"
 
 

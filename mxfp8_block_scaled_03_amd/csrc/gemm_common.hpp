@@ -1,0 +1,197 @@
+// gemm_common.hpp -- device helpers shared by the GEMM kernels (gemm_fp8.hip,
+// gemm_exact.hip, gemm_fallback.hip): operand and LDS plumbing, the scaled FP8 -> bf16
+// decode, the epilogue's SiLU and MX quantization of staged output rows, and the
+// XCD-aware tile order.
+//
+// "Low-Precision GPU Programming", "Scale ownership and the GEMM dataflow": Y = X W with the
+// product of the X-block and W-block scales inside the outer sum over 32-element K blocks;
+// the epilogue applies the scale (alpha), then bias, then an activation, then the cast, and a
+// producer epilogue may emit the MX codes and scales of its output for the next GEMM.
+#pragma once
+#include <type_traits>
+
+#include "codec.hpp"
+#include "internal.hpp"
+#include "mxblock.hpp"
+
+namespace mxq {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kGroupM = 4;   // tile rows per group in the tile order
+constexpr int kXcds = 8;     // accelerator complex dies (each with its own L2)
+
+extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+// Output tile of workgroup `wg`: consecutive workgroup ids go round-robin over the XCDs,
+// so tile t is given to the workgroups of one XCD first (neighbouring tiles share that
+// XCD's L2), then tiles are walked in groups of kGroupM tile rows, column by column.
+__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int ntiles = tiles_m * tiles_n;
+  const int xcd = wg % kXcds, local = wg / kXcds;
+  const int q = ntiles / kXcds, r = ntiles % kXcds;
+  const int t = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int per_group = kGroupM * tiles_n;
+  const int first_m = (t / per_group) * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  tm = first_m + (t % per_group) % gsize;
+  tn = (t % per_group) / gsize;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes of LDS at a lane address plus an offset that is a constant after unrolling
+// (folded into the ds_read_b128 immediate).
+__device__ __forceinline__ v4i lds16(uint32_t addr, int off) {
+  return *reinterpret_cast<const v4i*>(smem + addr + off);
+}
+
+// SiLU, x * sigmoid(x), in fp32 without an overflowing intermediate: with t = e^-|x|,
+// x / (1 + t) for x >= 0 and x * t / (1 + t) for x < 0.
+__device__ __forceinline__ float silu(float x) {
+  const float t = expf(-fabsf(x));
+  return x >= 0.0f ? x / (1.0f + t) : x * t / (1.0f + t);
+}
+
+
+// MX-quantize a wave's block of bf16 output values staged in LDS, along its rows: 128 rows
+// of 32 * NB values at LDS offset `base`, row pitch 64 * NB bytes, 16-byte chunk c of row r
+// stored at chunk c ^ (r & 7), values past column N staged as +0 (the zero padding of a
+// partial block).  Row r, block j becomes block blk0 + j of code row row0 + r ("Microscaling:
+// the two-row experiment": amax, power-of-two scale, RNE codes), written only when the row
+// is < M and the block < nbq.
+template <int NB>
+__device__ __forceinline__ void quantize_staged(uint32_t base, int lane, int row0, int M, int blk0, int nbq,
+                                                const GemmEpilogue& ep) {
+  constexpr int PITCH = 64 * NB;
+#pragma unroll 1
+  for (int it = 0; it < 2 * NB; ++it) {
+    const int p = 64 * it + lane, r = p / NB, j = p % NB;
+    mxblock::Chunk<1> ch[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t phys = (uint32_t)((4 * j + c) ^ (r & 7));
+      const v4i v = lds16(base + (uint32_t)(r * PITCH) + (phys << 4), 0);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) ch[c].w[w] = (uint32_t)v[w];
+    }
+    const int row = row0 + r, b = blk0 + j;
+    if (row < M && b < nbq) {
+      uint32_t amax = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t a = mxblock::chunk_abs_max<1>(ch[c]);
+        amax = amax > a ? amax : a;
+      }
+      uint32_t d[8], sb;
+      if (ep.q_fmt == kE4M3) {
+        sb = scale_byte_from_amax<kE4M3>(amax);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mxblock::encode_chunk<1, kE4M3>(ch[c], sb, d[2 * c], d[2 * c + 1]);
+      } else {
+        sb = scale_byte_from_amax<kE5M2>(amax);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mxblock::encode_chunk<1, kE5M2>(ch[c], sb, d[2 * c], d[2 * c + 1]);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(ep.qc + (int64_t)row * ep.ld_qc + 32 * (int64_t)b);
+      dst[0] = make_uint4(d[0], d[1], d[2], d[3]);
+      dst[1] = make_uint4(d[4], d[5], d[6], d[7]);
+      ep.qs[(int64_t)row * ep.ld_qs + b] = (uint8_t)sb;
+    }
+  }
+}
+
+// Keep the first `lim` bytes of a 16-byte fragment half, zero the rest.
+__device__ __forceinline__ v4i mask_bytes(v4i v, int lim) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    int keep = lim - 4 * d;
+    uint32_t m = keep >= 4 ? 0xFFFFFFFFu : (keep <= 0 ? 0u : ((1u << (8 * keep)) - 1u));
+    v[d] = (int)((uint32_t)v[d] & m);
+  }
+  return v;
+}
+
+
+// fp32 value 2^(byte-127) of an E8M0 byte (byte 0 is the fp32 subnormal 2^-127; 255 NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t byte) {
+  return __uint_as_float(byte == 0 ? 0x00400000u : (byte == 255 ? 0x7FC00000u : byte << 23));
+}
+
+// Eight codes (two dwords) -> eight bf16 values code * scale (exact while the product is
+// inside bf16's range), with the gfx950 scaled conversion.
+template <int F>
+__device__ __forceinline__ v8bf codes_to_bf16(uint32_t w0, uint32_t w1, float s) {
+  v2bf p0, p1, p2, p3;
+  if (F == kE4M3) {
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true);
+  } else {
+    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, s, false);
+    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, s, true);
+    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, s, false);
+    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, s, true);
+  }
+  typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+  v4bf lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  v4bf hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Exact-product accumulation: each lane decodes its codes with their block scale into
+// bf16 (exact) and feeds v_mfma_f32_32x32x16_bf16, whose products are exact and whose
+// sums are FP32.  Per 32-wide block, lane (i, g) holds k = 16g..16g+15 of the block:
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, v4i rsrc) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Raw buffer descriptor (stride 0) over [base, base + bytes), all fields wave-uniform.
+__device__ __forceinline__ v4i rsrc_of(uint64_t base, uint32_t bytes) {
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(base >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// s_waitcnt with vmcnt(n) and expcnt / lgkmcnt left at their maxima (n < 64).
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier ordering LDS accesses only (global DMA completion is handled by the
+// explicit vmcnt waits before it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+
+// Round-to-nearest-even float -> bf16 bits of two values, packed (lo = a).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+}
+
+}  // namespace
+}  // namespace mxq

@@ -65,6 +65,17 @@ struct GemmEpilogue {
   int q_fmt;
 };
 
+// The GEMM kernels (gemm_exact.hip, gemm_fp8.hip, gemm_fallback.hip); launch_gemm picks one.
+hipError_t launch_gemm_exact(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
+                             int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws,
+                             int64_t ld_ws, int w_fmt, const GemmEpilogue& ep, hipStream_t stream);
+hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
+                           int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
+                           int w_fmt, const GemmEpilogue& ep, hipStream_t stream);
+hipError_t launch_gemm_fallback(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
+                                int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws,
+                                int64_t ld_ws, int w_fmt, const GemmEpilogue& ep, int exact, hipStream_t stream);
+
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K,
                        const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_fmt,
                        const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws, int w_fmt,
