@@ -83,13 +83,21 @@ typedef enum {
  *                   accumulator then combine in FP32.  Error per output element
  *                   <= sum over groups g of 7 * 2^-12 * S_g * max_{k in g} |binade
  *                   products| + FP32 summation error.  Full MXFP8 matrix-core rate.
- * MXQ_ACC_FP32      every scaled product is formed exactly and summed in FP32: codes are
- *                   decoded with their block scale to bf16 in registers (exact while
- *                   each 2^(s-127) * code lies inside bf16's range, i.e. for scale
- *                   bytes roughly 10..245) and fed to v_mfma_f32_32x32x16_bf16, whose
- *                   products are exact and sums FP32.  Meets |y - y_exact| <= 1e-5 *
- *                   sum_k |scaled products| for ordinary data.  Half the FP8 matrix-core
- *                   rate at best.
+ * MXQ_ACC_FP32      exact products, FP32 sums.  Each code is decoded with its block scale
+ *                   to bfloat16, x~ = bf16(dec(code) * 2^(s-127)) (round to nearest even,
+ *                   bf16 subnormals kept; scale byte 255 gives NaN), and
+ *                   acc = sum_k x~ * w~ is formed by v_mfma_f32_32x32x16_bf16, whose
+ *                   products are exact (while they lie in FP32's normal range) and whose
+ *                   sums are FP32.  x~ is exactly dec(code) * 2^(s-127) for every code when
+ *                   3 <= s <= 246 (E4M3) or 10 <= s <= 239 (E5M2): the finest code bit
+ *                   (2^-9, 2^-16) times the scale reaches bf16's subnormal spacing 2^-133
+ *                   and the largest code (448, 57,344) times the scale stays below bf16's
+ *                   maximum.  The scale rule puts every block whose amax lies in
+ *                   [2^-116.2, 2^127.8] (E4M3) or [2^-102.2, 2^127.8] (E5M2) inside that
+ *                   window, so for such data the result meets |y - y_exact| <= 1e-5 *
+ *                   sum_k |scaled products| (plus the epilogue roundings).  Outside it the
+ *                   result is the exact-product FP32 sum of the bf16-rounded operands
+ *                   above.  Half the FP8 matrix-core rate at best.
  */
 typedef enum { MXQ_ACC_FP8_MFMA = 0, MXQ_ACC_FP32 = 1 } mxq_accum;
 
@@ -203,10 +211,16 @@ int mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales
  *          an [N][K] weight with MXQ_ROWWISE, or a [K][N] weight with MXQ_COLWISE);
  *          w_scales [N][ld_ws], w_elem MXQ_E4M3 or MXQ_E5M2 (mixed formats allowed).
  *          ld_x, ld_w >= Kp and multiples of 16; code pointers 16-byte aligned;
- *          ld_xs, ld_ws >= nb.  Performance: with MXQ_ACC_FP8_MFMA, scale arrays whose base
- *          and leading dimension are multiples of 16 bytes take the fastest kernel (the
- *          other layouts are handled by a slower one); a 16-byte aligned y with a 16-byte
- *          multiple row pitch gets full-row stores.
+ *          ld_xs, ld_ws >= nb.  Bytes past nb of a scale row are ignored, but may be
+ *          read: the MXQ_ACC_FP32 kernel reads rows other than the last in 4-byte words
+ *          (never past ld), and with MXQ_ACC_FP8_MFMA and 16-byte aligned scale rows
+ *          every row, the last included, is read in 16-byte units, so the last scale
+ *          row must then be addressable up to 16 * ceil(nb / 16) bytes (mxq_quantize's
+ *          torch wrapper allocates scale rows padded to 16 bytes).
+ *          Performance: scale arrays whose base and leading dimension are multiples of
+ *          4 bytes (MXQ_ACC_FP32) or 16 bytes (MXQ_ACC_FP8_MFMA) take the fastest
+ *          kernel of their mode (other layouts a slower one); a 16-byte aligned y with
+ *          a 16-byte multiple row pitch gets full-row stores.
  * Result   acc[i][j] = sum_b 2^(sx[i][b] + sw[j][b] - 254) * sum_{k in b, k < K}
  *                        dec(x[i][k]) * dec(w[j][k])
  *          accumulated as `accum` states (see mxq_accum; summation order is

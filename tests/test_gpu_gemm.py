@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import mxfp8_block_scaled_03_amd as mxq
+import oracle
 from mxfp8_block_scaled_03_amd import workloads as wl
 from gpu_helpers import full_check, sampled_check, say
 
@@ -207,3 +208,76 @@ def test_workload1_full(accum):
     y = mxq.gemm(xc, xs, wc, ws, d["K"], out_dtype=torch.float32, accum=accum)
     full_check(xc, xs, "e4m3", wc, ws, "e4m3", d["K"], y, torch.float32, what="workload1 " + accum,
                strict=accum == "fp32")
+
+
+# ----------------------------------------------------------------- exact mode at extreme scale bytes
+
+# Scale-byte windows inside which every code * 2^(s-127) is a bfloat16 value (E4M3: the finest
+# code bit 2^-9 must reach bf16's subnormal spacing 2^-133 and 448 * 2^(s-127) must stay below
+# bf16's maximum; E5M2: finest bit 2^-16, maximum 57,344)
+EXACT_WINDOW = {"e4m3": (3, 246), "e5m2": (10, 239)}
+
+
+def quantized_fp32(rng, rows, K, scale, fmt, dist="normal"):
+    v = rng.standard_normal((rows, K)) if dist == "normal" else rng.uniform(-1, 1, (rows, K))
+    x = torch.from_numpy((v * scale).astype(np.float32)).to(DEV)
+    return mxq.quantize(x, fmt, "row")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("case", ["huge", "tiny_inside", "tiny_outside"])
+def test_exact_mode_at_extreme_scale_bytes(fmt, case):
+    """The exact-product mode multiplies bf16 roundings of code * 2^(s-127).  Inside the
+    window of EXACT_WINDOW those are the exact decoded values, so outputs meet the strict
+    bound against the FP64 oracle: X near 1e36 (scale bytes ~233-240) and X near the small end
+    of the window.  Outside it (X near 1e-36: scale bytes 0..2) the result is the exact-product
+    FP32 sum of the bf16-rounded operands (the oracle's bf16 dequantization, bf16 subnormals
+    kept), within 1e-5 of the sum of their absolute products.  W is scaled so that every
+    product stays in FP32's normal range."""
+    rng = np.random.default_rng(40 + len(case))
+    M, N, K = 160, 144, 480
+    lo, hi = EXACT_WINDOW[fmt]
+    xmag = {"huge": 1e36, "tiny_inside": 2.0 ** (-104 if fmt == "e4m3" else -96), "tiny_outside": 1e-36}[case]
+    wmag = {"huge": 0.02, "tiny_inside": 1.0, "tiny_outside": 2.0 ** 40}[case]
+    xc, xs = quantized_fp32(rng, M, K, xmag, fmt)
+    wc, ws = quantized_fp32(rng, N, K, wmag, "e4m3")
+    xs_h = xs.cpu().numpy()
+    inside = (xs_h >= lo) & (xs_h <= hi)
+    say("extreme scales %s %s: X scale bytes %d..%d" % (fmt, case, xs_h.min(), xs_h.max()))
+    y = mxq.gemm(xc, xs, wc, ws, K, fmt, "e4m3", out_dtype=torch.float32, accum="fp32")
+    torch.cuda.synchronize()
+    if case != "tiny_outside":
+        assert inside.all(), "the inputs do not stay inside the exact window"
+        full_check(xc, xs, fmt, wc, ws, "e4m3", K, y, torch.float32, what="exact %s %s" % (fmt, case), strict=True)
+        return
+    assert not inside.any(), "the inputs do not leave the exact window"
+    xq = oracle.dequantize(xc.cpu().numpy(), xs_h, fmt, K, out="bf16").astype(np.uint32) << 16
+    wq = oracle.dequantize(wc.cpu().numpy(), ws.cpu().numpy(), "e4m3", K, out="bf16").astype(np.uint32) << 16
+    xb = xq.view(np.float32).astype(np.float64)
+    wb = wq.view(np.float32).astype(np.float64)
+    prod_min = np.min(np.abs(xb[xb != 0])) * np.min(np.abs(wb[wb != 0]))
+    assert prod_min >= 2.0 ** -126, "a product leaves FP32's normal range"
+    ref = xb @ wb.T
+    t = np.abs(xb) @ np.abs(wb).T
+    err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= 1e-5 * t), "worst |err|/T = %g" % float(np.max(err / t))
+    # the rounding is real: the exact decoded operands give a different sum somewhere
+    y_exact, _ = oracle.gemm(xc.cpu().numpy(), xs_h, fmt, wc.cpu().numpy(), ws.cpu().numpy(), "e4m3", K)
+    assert np.any(np.abs(ref - y_exact) > 0)
+
+
+def test_exact_mode_nan_scale_gives_nan():
+    """A block holding Inf quantizes to scale byte 255 with NaN codes; every output of that
+    row is NaN in the exact-product mode, the others are finite and meet the strict bound."""
+    rng = np.random.default_rng(47)
+    M, N, K = 96, 80, 256
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(DEV)
+    x[5, 70] = float("inf")
+    xc, xs = mxq.quantize(x, "e4m3", "row")
+    wc, ws = quantized_fp32(rng, N, K, 0.02, "e4m3")
+    assert int(xs[5, 2]) == 255
+    y = mxq.gemm(xc, xs, wc, ws, K, out_dtype=torch.float32, accum="fp32").cpu()
+    assert torch.isnan(y[5]).all()
+    keep = torch.ones(M, dtype=torch.bool)
+    keep[5] = False
+    assert torch.isfinite(y[keep]).all()
