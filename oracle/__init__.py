@@ -79,6 +79,11 @@ def lib():
         L.mxo_encode.argtypes = [ctypes.c_double, ctypes.c_int]
         L.mxo_scale_byte.restype = ctypes.c_int
         L.mxo_scale_byte.argtypes = [ctypes.c_double, ctypes.c_int]
+        L.mxo_scale_byte_ocp.restype = ctypes.c_int
+        L.mxo_scale_byte_ocp.argtypes = [ctypes.c_double, ctypes.c_int]
+        L.mxo_quantize_rule.restype = None
+        L.mxo_quantize_rule.argtypes = [vp, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        vp, i64, vp, i64]
         L.mxo_num_finite_codes.restype = ctypes.c_int
         L.mxo_num_finite_codes.argtypes = [ctypes.c_int]
         L.mxo_num_threads.restype = ctypes.c_int
@@ -153,12 +158,22 @@ def _src_type(src: np.ndarray) -> int:
     raise TypeError("src must be float32 or uint16 (bf16 bits), got %s" % src.dtype)
 
 
-def quantize(src: np.ndarray, fmt: str, axis: int = 0):
+RULE = {"ceil": 0, "ocp": 1}
+
+
+def scale_byte_ocp(amax: float, fmt: str) -> int:
+    """E8M0 byte of the OCP MX scale rule: floor(log2(amax)) - emax_elem, clamped at -127."""
+    return lib().mxo_scale_byte_ocp(float(amax), FMT[fmt])
+
+
+def quantize(src: np.ndarray, fmt: str, axis: int = 0, rule: str = "ceil"):
     """Quantize a 2-D array (float32, or uint16 holding bf16 bits).
 
     axis=0: 1x32 groups along each row; returns codes [rows][Kp], scales [rows][Kp/32].
     axis=1: 32x1 groups down each column, stored transposed: codes [cols][Kp], scales
             [cols][Kp/32] with K = rows.
+    rule="ceil": the pages' scale rule (amax/fmax rounded up to a power of two);
+    rule="ocp": the OCP MX specification's rule (floor(log2(amax)) - emax_elem, satfinite).
     """
     src = np.ascontiguousarray(src)
     rows, cols = src.shape
@@ -167,8 +182,8 @@ def quantize(src: np.ndarray, fmt: str, axis: int = 0):
     codes = np.zeros((L, max(Kp, 1)), dtype=np.uint8)
     scales = np.zeros((L, max(Kp // 32, 1)), dtype=np.uint8)
     if L > 0 and K > 0:
-        lib().mxo_quantize(_ptr(src), _src_type(src), rows, cols, cols, axis, FMT[fmt],
-                           _ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1])
+        lib().mxo_quantize_rule(_ptr(src), _src_type(src), rows, cols, cols, axis, FMT[fmt], RULE[rule],
+                                _ptr(codes), codes.shape[1], _ptr(scales), scales.shape[1])
     return codes[:, :Kp], scales[:, :Kp // 32]
 
 

@@ -147,14 +147,37 @@ def scale_exponent(amax: Fraction, fmt: str) -> int:
     return max(-127, ceil_log2(amax / FORMATS[fmt][3]))
 
 
-def quantize_block(values, fmt: str, negzero=None):
+def largest_normal_exponent(fmt: str) -> int:
+    """Exponent E of the format's largest finite value written 1.f * 2^E, from its code."""
+    top = max(v for _, v in _MAGS[fmt])
+    E = 0
+    while Fraction(2) ** (E + 1) <= top:
+        E += 1
+    return E
+
+
+def scale_exponent_ocp(amax: Fraction, fmt: str) -> int:
+    """The OCP MX rule: floor(log2(amax)) - (exponent of the largest normal), at least -127;
+    0 for a zero block.  floor(log2) by comparing powers of two, exactly."""
+    if amax == 0:
+        return 0
+    E = 0
+    while Fraction(2) ** E > amax:
+        E -= 1
+    while Fraction(2) ** (E + 1) <= amax:
+        E += 1
+    return max(-127, E - largest_normal_exponent(fmt))
+
+
+def quantize_block(values, fmt: str, negzero=None, rule: str = "ceil"):
     """Quantize a list of <= 32 exact rationals (one MX block, zero-padded to 32).
 
-    ``negzero[i]`` marks value i as -0.  Returns (codes[32], scale_byte).
+    ``negzero[i]`` marks value i as -0.  ``rule`` picks the scale exponent ("ceil": the
+    pages', "ocp": the OCP MX specification's).  Returns (codes[32], scale_byte).
     """
     assert len(values) <= 32
     amax = max((abs(v) for v in values), default=Fraction(0))
-    e = scale_exponent(amax, fmt)
+    e = scale_exponent(amax, fmt) if rule == "ceil" else scale_exponent_ocp(amax, fmt)
     S = Fraction(2) ** e
     codes = []
     for i in range(32):

@@ -22,7 +22,9 @@
  *       reconstruction scale, x_hat = S*q, q = Q(x/S); a zero-only group takes S = 1.
  *     - "Microscaling: the two-row experiment": 32-element blocks, E8M0 byte c means
  *       2^(c-127), 255 is NaN; the conservative power-of-two scale rounds amax/448
- *       upward (exponent = max(-127, ceil(log2(amax/fmax)))), zero block -> 1.
+ *       upward (exponent = max(-127, ceil(log2(amax/fmax)))), zero block -> 1; the OCP
+ *       MX specification describes another scale-selection algorithm (the page names it
+ *       without stating it; it is taken from the specification, see mxo_scale_byte_ocp).
  *
  * Readings where the pages are silent (each is listed with its reason in the design notes):
  *   - E5M2 uses the same scale rule with fmax = 57,344.
@@ -238,6 +240,30 @@ int mxo_scale_byte(double amax, int fmt)
     return e + 127;
 }
 
+/* Scale rule of the OCP Microscaling Formats (MX) Specification v1.0, which the pages
+ * cite as the other scale-selection algorithm [LPGP "Microscaling: the two-row
+ * experiment"]: the shared exponent is floor(log2(amax)) minus the exponent of the element
+ * format's largest normal (E4M3: 448 = 1.75 * 2^8 -> 8; E5M2: 57,344 = 1.75 * 2^15 -> 15),
+ * and the elements are then converted with round-to-nearest-even, values past the largest
+ * normal clamped to it (satfinite).  Readings shared with the rule above: the exponent is
+ * clamped at -127 (E8M0's smallest), a zero block takes S = 1, a non-finite block 255.
+ * floor(log2(amax)) is the literal search for the largest E with 2^E <= amax (exact in
+ * FP64 for every fp32 / bf16 amax).                                                     */
+int mxo_scale_byte_ocp(double amax, int fmt)
+{
+    if (!isfinite(amax)) return 255;
+    if (amax == 0.0) return 127;
+    int emax_elem = fmt == MXO_FMT_E4M3 ? 8 : 15;
+    int E = -150;                                 /* 2^-150 is below every fp32 value */
+    while (ldexp(1.0, E + 1) <= amax) ++E;
+    int e = E - emax_elem;
+    if (e < -127) e = -127;
+    return e + 127;
+}
+
+#define MXO_RULE_CEIL 0
+#define MXO_RULE_OCP 1
+
 /* ---------------------------------------------------------------- helpers --------- */
 
 static double load_elem(const void *src, int src_type, int64_t idx)
@@ -293,7 +319,8 @@ static float to_f32(double v)
  * blocks [LPGP "Scale ownership and the GEMM dataflow": block index b along K; partial
  * final block zero-padded].                                                              */
 static void quantize_line(const void *src, int src_type, int64_t base, int64_t stride, int64_t K,
-                          int fmt, uint8_t *codes, uint8_t *scales, int sr, uint64_t seed, int64_t n0)
+                          int fmt, uint8_t *codes, uint8_t *scales, int sr, uint64_t seed, int64_t n0,
+                          int rule)
 {
     int64_t nb = (K + 31) / 32;
     for (int64_t b = 0; b < nb; ++b) {
@@ -310,7 +337,7 @@ static void quantize_line(const void *src, int src_type, int64_t base, int64_t s
             for (int64_t k = k0; k < k0 + 32; ++k) codes[k] = 0x7F;
             continue;
         }
-        int sb = mxo_scale_byte(amax, fmt);
+        int sb = rule == MXO_RULE_OCP ? mxo_scale_byte_ocp(amax, fmt) : mxo_scale_byte(amax, fmt);
         scales[b] = (uint8_t)sb;
         int e = sb - 127;
         for (int64_t k = k0; k < k0 + 32; ++k) {
@@ -332,7 +359,7 @@ static void quantize_line(const void *src, int src_type, int64_t base, int64_t s
  * Writes Kp = 32*ceil(K/32) codes and Kp/32 scale bytes per line.                        */
 static void quantize_any(const void *src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
                          int axis, int fmt, uint8_t *codes, int64_t ld_codes, uint8_t *scales,
-                         int64_t ld_scales, int sr, uint64_t seed)
+                         int64_t ld_scales, int sr, uint64_t seed, int rule)
 {
     build_tables();
     int64_t L = axis == 0 ? rows : cols;
@@ -343,7 +370,7 @@ static void quantize_any(const void *src, int src_type, int64_t rows, int64_t co
         int64_t base = axis == 0 ? l * ld_src : l;
         int64_t stride = axis == 0 ? 1 : ld_src;
         quantize_line(src, src_type, base, stride, K, fmt, codes + l * ld_codes,
-                      scales + l * ld_scales, sr, seed, l * Kp);
+                      scales + l * ld_scales, sr, seed, l * Kp, rule);
     }
 }
 
@@ -351,7 +378,16 @@ void mxo_quantize(const void *src, int src_type, int64_t rows, int64_t cols, int
                   int axis, int fmt, uint8_t *codes, int64_t ld_codes, uint8_t *scales,
                   int64_t ld_scales)
 {
-    quantize_any(src, src_type, rows, cols, ld_src, axis, fmt, codes, ld_codes, scales, ld_scales, 0, 0);
+    quantize_any(src, src_type, rows, cols, ld_src, axis, fmt, codes, ld_codes, scales, ld_scales, 0, 0,
+                 MXO_RULE_CEIL);
+}
+
+/* mxo_quantize with the scale rule chosen: 0 the pages' (ceil), 1 the OCP MX rule.       */
+void mxo_quantize_rule(const void *src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
+                       int axis, int fmt, int rule, uint8_t *codes, int64_t ld_codes, uint8_t *scales,
+                       int64_t ld_scales)
+{
+    quantize_any(src, src_type, rows, cols, ld_src, axis, fmt, codes, ld_codes, scales, ld_scales, 0, 0, rule);
 }
 
 /* The same blocks and scales with stochastically rounded codes (the readings above give
@@ -360,7 +396,8 @@ void mxo_quantize_sr(const void *src, int src_type, int64_t rows, int64_t cols, 
                      int axis, int fmt, uint64_t seed, uint8_t *codes, int64_t ld_codes,
                      uint8_t *scales, int64_t ld_scales)
 {
-    quantize_any(src, src_type, rows, cols, ld_src, axis, fmt, codes, ld_codes, scales, ld_scales, 1, seed);
+    quantize_any(src, src_type, rows, cols, ld_src, axis, fmt, codes, ld_codes, scales, ld_scales, 1, seed,
+                 MXO_RULE_CEIL);
 }
 
 /* Quantize with caller-owned scale bytes [LPGP "Worked failure: stale delayed scale": a
