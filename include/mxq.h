@@ -126,6 +126,33 @@ int mxq_quantize(const void* src, int src_type, int64_t rows, int64_t cols, int6
                  int64_t ld_scales, void* stream);
 
 /*
+ * mxq_scale_rule -- how a block's E8M0 scale is chosen from its amax.
+ * MXQ_SCALE_CEIL  the rule of "Low-Precision GPU Programming", "Microscaling: the two-row
+ *                 experiment": e is the smallest integer >= -127 with amax <= fmax * 2^e
+ *                 (amax / fmax rounded up to a power of two), so no code saturates.  The
+ *                 rule mxq_quantize and every other quantizing entry point use.
+ * MXQ_SCALE_OCP   the scale-selection algorithm of the OCP Microscaling Formats (MX)
+ *                 Specification v1.0, which the same section names as the alternative:
+ *                 e = floor(log2 amax) - emax_elem (emax_elem = 8 for E4M3, 15 for E5M2,
+ *                 the exponent of fmax), clamped at -127.  It is one below the CEIL
+ *                 exponent exactly when amax's significand exceeds 1.75, and then the
+ *                 codes of values above fmax * 2^e saturate to +-fmax (RNE-satfinite).
+ * Both: a zero block takes scale byte 127, a block holding NaN or Inf byte 255 (codes 0x7F).
+ */
+typedef enum { MXQ_SCALE_CEIL = 0, MXQ_SCALE_OCP = 1 } mxq_scale_rule;
+
+/*
+ * mxq_quantize_rule -- mxq_quantize with the scale rule chosen.
+ * All arguments as for mxq_quantize, plus rule (mxq_scale_rule; MXQ_ERR_ARG for any other
+ * value).  rule = MXQ_SCALE_CEIL is mxq_quantize itself.  Per block: scale byte from the
+ * rule above, code = RNE-satfinite(x * 2^-e) with the sign copied; bit-exact and
+ * independent of the launch configuration, like mxq_quantize.
+ */
+int mxq_quantize_rule(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src,
+                      int axis, int elem, int rule, uint8_t* codes, int64_t ld_codes,
+                      uint8_t* scales, int64_t ld_scales, void* stream);
+
+/*
  * mxq_quantize_sr -- mxq_quantize with stochastically rounded codes (gradients).
  * ("Rounding: RNE versus stochastic rounding": between the neighbouring representable
  * values l <= x < u, round up with probability (x - l) / (u - l), so E[SR(x)] = x and

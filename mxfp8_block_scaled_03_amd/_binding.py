@@ -11,11 +11,13 @@ MXQ_F32, MXQ_BF16, MXQ_E4M3, MXQ_E5M2 = 0, 1, 2, 3
 MXQ_ROWWISE, MXQ_COLWISE = 0, 1
 MXQ_ACC_FP8_MFMA, MXQ_ACC_FP32 = 0, 1
 MXQ_ACT_NONE, MXQ_ACT_SILU = 0, 1
+MXQ_SCALE_CEIL, MXQ_SCALE_OCP = 0, 1
 
 _ELEM = {"e4m3": MXQ_E4M3, "e5m2": MXQ_E5M2}
 _ACC = {"fp8": MXQ_ACC_FP8_MFMA, "fp32": MXQ_ACC_FP32}
 _ACT = {None: MXQ_ACT_NONE, "none": MXQ_ACT_NONE, "silu": MXQ_ACT_SILU}
 _AXIS = {"row": MXQ_ROWWISE, "col": MXQ_COLWISE, 0: MXQ_ROWWISE, 1: MXQ_COLWISE}
+_RULE = {"ceil": MXQ_SCALE_CEIL, "ocp": MXQ_SCALE_OCP}
 
 
 class MxqError(ValueError):
@@ -44,6 +46,8 @@ def lib():
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.mxq_quantize.restype = ci
         L.mxq_quantize.argtypes = [vp, ci, i64, i64, i64, ci, ci, vp, i64, vp, i64, vp]
+        L.mxq_quantize_rule.restype = ci
+        L.mxq_quantize_rule.argtypes = [vp, ci, i64, i64, i64, ci, ci, ci, vp, i64, vp, i64, vp]
         L.mxq_quantize_sr.restype = ci
         L.mxq_quantize_sr.argtypes = [vp, ci, i64, i64, i64, ci, ci, ctypes.c_uint64, vp, i64, vp, i64, vp]
         L.mxq_quantize_scaled.restype = ci
@@ -72,6 +76,12 @@ def mxq_quantize(src, src_type, rows, cols, ld_src, axis, elem, codes, ld_codes,
                  stream=None) -> int:
     return lib().mxq_quantize(src, src_type, rows, cols, ld_src, axis, elem, codes, ld_codes, scales,
                               ld_scales, stream)
+
+
+def mxq_quantize_rule(src, src_type, rows, cols, ld_src, axis, elem, rule, codes, ld_codes, scales, ld_scales,
+                      stream=None) -> int:
+    return lib().mxq_quantize_rule(src, src_type, rows, cols, ld_src, axis, elem, rule, codes, ld_codes, scales,
+                                   ld_scales, stream)
 
 
 def mxq_quantize_sr(src, src_type, rows, cols, ld_src, axis, elem, seed, codes, ld_codes, scales, ld_scales,
@@ -190,7 +200,7 @@ def _ld(t) -> int:
     return t.stride(0) if t.shape[0] > 0 and t.stride(0) >= t.shape[1] else max(t.shape[1], 1)
 
 
-def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None):
+def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None, rule: str = "ceil"):
     """MX-quantize a 2-D bf16/fp32 CUDA tensor.
 
     axis="row": 1x32 groups along each row -> codes [rows][Kp], scales [rows][Kp/32].
@@ -200,11 +210,15 @@ def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None):
     outputs may be wider than Kp (their row stride is passed as the leading dimension).
     Scales allocated here are a [L][Kp/32] view of rows padded to a multiple of 16 bytes,
     the layout the fastest GEMM kernel reads.
+    rule="ceil": the pages' scale rule (mxq_quantize); rule="ocp": the OCP MX
+    specification's (floor(log2 amax) - emax, satfinite codes), via mxq_quantize_rule.
     """
     torch = _torch()
     _req_wide(x, "x")
     if axis not in _AXIS or elem not in _ELEM:
         raise ValueError("axis must be 'row' or 'col' and elem 'e4m3' or 'e5m2'")
+    if rule not in _RULE:
+        raise ValueError("rule must be 'ceil' or 'ocp'")
     rows, cols = x.shape
     ax = _AXIS[axis]
     L, K = (rows, cols) if ax == MXQ_ROWWISE else (cols, rows)
@@ -219,10 +233,16 @@ def quantize(x, elem: str = "e4m3", axis="row", codes=None, scales=None):
         codes = torch.empty((L, Kp), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((L, _round_up(nb, 16)), dtype=torch.uint8, device=x.device)[:, :nb]
-    st = mxq_quantize(x.data_ptr(), _wide_type(x), rows, cols, _ld(x), ax,
-                      _ELEM[elem], codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales),
-                      _stream_handle())
-    _check(st, "mxq_quantize")
+    if rule == "ceil":
+        st = mxq_quantize(x.data_ptr(), _wide_type(x), rows, cols, _ld(x), ax,
+                          _ELEM[elem], codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales),
+                          _stream_handle())
+        _check(st, "mxq_quantize")
+    else:
+        st = mxq_quantize_rule(x.data_ptr(), _wide_type(x), rows, cols, _ld(x), ax, _ELEM[elem],
+                               _RULE[rule], codes.data_ptr(), _ld(codes), scales.data_ptr(), _ld(scales),
+                               _stream_handle())
+        _check(st, "mxq_quantize_rule")
     return codes, scales
 
 

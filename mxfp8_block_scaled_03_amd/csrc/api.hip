@@ -15,6 +15,7 @@ constexpr int64_t kMaxCodeLd = (int64_t)1 << 24; // GEMM code leading dims (32-b
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 int to_fmt(int elem) { return elem == MXQ_E4M3 ? mxq::kE4M3 : mxq::kE5M2; }
+int to_rule(int rule) { return rule == MXQ_SCALE_OCP ? mxq::kRuleOcp : mxq::kRuleCeil; }
 
 bool is_elem(int t) { return t == MXQ_E4M3 || t == MXQ_E5M2; }
 bool is_wide(int t) { return t == MXQ_F32 || t == MXQ_BF16; }
@@ -42,12 +43,19 @@ const char* mxq_status_string(int status) {
   }
 }
 
-int mxq_version(void) { return 100; }
+int mxq_version(void) { return 101; }
 
 int mxq_quantize(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int axis, int elem,
                  uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, void* stream) {
+  return mxq_quantize_rule(src, src_type, rows, cols, ld_src, axis, elem, MXQ_SCALE_CEIL, codes, ld_codes, scales,
+                           ld_scales, stream);
+}
+
+int mxq_quantize_rule(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int axis, int elem,
+                      int rule, uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, void* stream) {
   if (!is_wide(src_type) || !is_elem(elem)) return MXQ_ERR_DTYPE;
   if (axis != MXQ_ROWWISE && axis != MXQ_COLWISE) return MXQ_ERR_ARG;
+  if (rule != MXQ_SCALE_CEIL && rule != MXQ_SCALE_OCP) return MXQ_ERR_ARG;
   if (rows < 0 || cols < 0 || rows >= kMaxDim || cols >= kMaxDim) return MXQ_ERR_SHAPE;
   const int64_t L = axis == MXQ_ROWWISE ? rows : cols;
   const int64_t K = axis == MXQ_ROWWISE ? cols : rows;
@@ -63,11 +71,11 @@ int mxq_quantize(const void* src, int src_type, int64_t rows, int64_t cols, int6
   if (axis == MXQ_ROWWISE) {
     const bool vec = src16 && K % 8 == 0;
     const bool flat = vec && ld_src == K && K % 32 == 0 && ld_codes == Kp && ld_scales == nb;
-    return hip_status(mxq::launch_quant_rows(src, src_type == MXQ_BF16, rows, K, ld_src, to_fmt(elem), codes,
-                                             ld_codes, scales, ld_scales, flat, vec, st));
+    return hip_status(mxq::launch_quant_rows(src, src_type == MXQ_BF16, rows, K, ld_src, to_fmt(elem), to_rule(rule),
+                                             codes, ld_codes, scales, ld_scales, flat, vec, st));
   }
-  return hip_status(mxq::launch_quant_cols(src, src_type == MXQ_BF16, rows, cols, ld_src, to_fmt(elem), codes,
-                                           ld_codes, scales, ld_scales, src16, st));
+  return hip_status(mxq::launch_quant_cols(src, src_type == MXQ_BF16, rows, cols, ld_src, to_fmt(elem), to_rule(rule),
+                                           codes, ld_codes, scales, ld_scales, src16, st));
 }
 
 int mxq_quantize_sr(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int axis, int elem,

@@ -52,6 +52,30 @@ __device__ __forceinline__ uint32_t scale_byte_from_amax(uint32_t abits) {
   return eb == 0 ? 0u : (uint32_t)(byte < 0 ? 0 : byte);
 }
 
+// E8M0 scale byte under the scale rule of the OCP Microscaling Formats (MX) Specification
+// v1.0, which "Low-Precision GPU Programming", "Microscaling: the two-row experiment" names
+// as the other scale-selection algorithm: e = floor(log2 amax) - emax, clamped at -127.  For a normal
+// amax floor(log2 amax) is its unbiased exponent, so the byte is eb - emax clamped at 0;
+// a subnormal amax always clamps.  Zero -> 127, Inf/NaN -> 255, as for the pages' rule.
+// The scaled values can then exceed fmax (by less than a factor 8/7); the encoder
+// saturates them (satfinite).
+template <int F>
+__device__ __forceinline__ uint32_t scale_byte_ocp(uint32_t abits) {
+  if (abits >= 0x7F800000u) return 255u;
+  if (abits == 0u) return 127u;
+  const int byte = (int)(abits >> 23) - Fp8<F>::emax;
+  return byte < 0 ? 0u : (uint32_t)byte;
+}
+
+// Scale rule selector: kRuleCeil is the pages' rule (amax / fmax rounded up to a power of
+// two), kRuleOcp the specification's (floor(log2 amax) - emax, satfinite codes).
+enum : int { kRuleCeil = 0, kRuleOcp = 1 };
+
+template <int F, int R>
+__device__ __forceinline__ uint32_t scale_byte_rule(uint32_t abits) {
+  return R == kRuleOcp ? scale_byte_ocp<F>(abits) : scale_byte_from_amax<F>(abits);
+}
+
 // fp32 value of 2^-e for a finite scale byte (e = byte - 127, byte in [0, 254]):
 // the biased exponent of 2^-e is 127 - e = 254 - byte, which stays in [1, 254] for
 // every byte the scale rule can produce from finite data (byte <= 247).

@@ -10,15 +10,16 @@ int device_cu_count();
 
 // Rowwise quantize: line l = row l of src, K = cols.  flat: the whole problem is one
 // dense run of blocks (ld_src == K == Kp, ld_codes == Kp, ld_scales == nb).
-// vec: every 8-element chunk of src can be read with 16-byte loads.
+// vec: every 8-element chunk of src can be read with 16-byte loads.  rule: the scale
+// rule, kRuleCeil (0, the pages') or kRuleOcp (1, the OCP MX specification's).
 hipError_t launch_quant_rows(const void* src, int src_bf16, int64_t rows, int64_t K, int64_t ld_src,
-                             int fmt, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                             int fmt, int rule, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
                              int64_t ld_scales, bool flat, bool vec, hipStream_t stream);
 
 // Columnwise quantize: line l = column l of src [rows][ld_src], K = rows, codes and
 // scales stored [cols][ld].
 hipError_t launch_quant_cols(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src,
-                             int fmt, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                             int fmt, int rule, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
                              int64_t ld_scales, bool vec, hipStream_t stream);
 
 // Both orientations in one pass: rowwise codes [rows][ld_rc] (K = cols) and columnwise

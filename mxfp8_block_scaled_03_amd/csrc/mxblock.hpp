@@ -74,10 +74,32 @@ __device__ __forceinline__ uint32_t value_bits(const Chunk<SRC_BF16>& c, int i) 
   return c.w[i];
 }
 
+// Magnitude caps at fmax * S for a finite scale byte sb (1..254) whose fmax * S is a
+// normal number (sb + emax <= 254, which every byte of a finite block meets): fmax is
+// 1.75 * 2^emax in both formats, so the cap's significand bits are 0x60 (bf16) /
+// 0x600000 (fp32).  Clamping |x| to the cap before the hardware conversion makes it
+// saturate: RNE(cap / S) = fmax, and any |x| <= cap converts as before.  Only the OCP
+// scale rule needs it; under the pages' rule |x| <= cap holds already.
+template <int F>
+__device__ __forceinline__ uint32_t clamp_pk_bf16(uint32_t w, uint32_t sb) {
+  const uint32_t cap = ((sb + (uint32_t)Fp8<F>::emax) << 7) | 0x60u;
+  const v2u16 m = __builtin_elementwise_min(__builtin_bit_cast(v2u16, w & 0x7FFF7FFFu),
+                                            __builtin_bit_cast(v2u16, cap | (cap << 16)));
+  return __builtin_bit_cast(uint32_t, m) | (w & 0x80008000u);
+}
+
+template <int F>
+__device__ __forceinline__ uint32_t clamp_f32(uint32_t w, uint32_t sb) {
+  const uint32_t cap = ((sb + (uint32_t)Fp8<F>::emax) << 23) | 0x600000u;
+  const uint32_t m = w & 0x7FFFFFFFu;
+  return (m < cap ? m : cap) | (w & 0x80000000u);
+}
+
 // Codes of the 8 values of a chunk under scale byte sb (1..254: hardware conversion;
 // 0: software RNE after multiplying by 2^127, exact for such tiny blocks; 255: NaN
-// block, all 0x7F).  Returns 8 code bytes in two dwords.
-template <int SRC_BF16, int F>
+// block, all 0x7F).  Returns 8 code bytes in two dwords.  R = kRuleOcp clamps the
+// magnitudes to fmax * S first (the software encoder saturates by itself).
+template <int SRC_BF16, int F, int R = kRuleCeil>
 __device__ __forceinline__ void encode_chunk(const Chunk<SRC_BF16>& c, uint32_t sb, uint32_t& d0, uint32_t& d1) {
   if (sb == 255u) {
     d0 = d1 = 0x7F7F7F7Fu;
@@ -92,16 +114,49 @@ __device__ __forceinline__ void encode_chunk(const Chunk<SRC_BF16>& c, uint32_t 
     return;
   }
   const float scale = __uint_as_float(sb << 23);  // 2^(sb-127)
+  Chunk<SRC_BF16> x = c;
+  if (R == kRuleOcp) {
+#pragma unroll
+    for (int i = 0; i < (SRC_BF16 ? 4 : 8); ++i) x.w[i] = SRC_BF16 ? clamp_pk_bf16<F>(c.w[i], sb) : clamp_f32<F>(c.w[i], sb);
+  }
   if (SRC_BF16) {
-    d0 = cvt2_bf16<F>(0u, c.w[0], scale, false);
-    d0 = cvt2_bf16<F>(d0, c.w[1], scale, true);
-    d1 = cvt2_bf16<F>(0u, c.w[2], scale, false);
-    d1 = cvt2_bf16<F>(d1, c.w[3], scale, true);
+    d0 = cvt2_bf16<F>(0u, x.w[0], scale, false);
+    d0 = cvt2_bf16<F>(d0, x.w[1], scale, true);
+    d1 = cvt2_bf16<F>(0u, x.w[2], scale, false);
+    d1 = cvt2_bf16<F>(d1, x.w[3], scale, true);
   } else {
-    d0 = cvt2_f32<F>(0u, c.w[0], c.w[1], scale, false);
-    d0 = cvt2_f32<F>(d0, c.w[2], c.w[3], scale, true);
-    d1 = cvt2_f32<F>(0u, c.w[4], c.w[5], scale, false);
-    d1 = cvt2_f32<F>(d1, c.w[6], c.w[7], scale, true);
+    d0 = cvt2_f32<F>(0u, x.w[0], x.w[1], scale, false);
+    d0 = cvt2_f32<F>(d0, x.w[2], x.w[3], scale, true);
+    d1 = cvt2_f32<F>(0u, x.w[4], x.w[5], scale, false);
+    d1 = cvt2_f32<F>(d1, x.w[6], x.w[7], scale, true);
+  }
+}
+
+// Codes of a 32-value block held as fp32 bit patterns (the columnwise kernels' layout)
+// under scale byte sb, with the same three cases and the same clamp as encode_chunk.
+template <int F, int R = kRuleCeil>
+__device__ __forceinline__ void encode_block32(const uint32_t v[32], uint32_t sb, uint32_t out[8]) {
+  if (sb == 255u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = 0x7F7F7F7Fu;
+  } else if (sb == 0u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w |= encode_rne_sat<F>(__uint_as_float(v[4 * i + j]) * 0x1p127f) << (8 * j);
+      out[i] = w;
+    }
+  } else {
+    const float scale = __uint_as_float(sb << 23);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = R == kRuleOcp ? clamp_f32<F>(v[4 * i + j], sb) : v[4 * i + j];
+      const uint32_t w = cvt2_f32<F>(0u, a[0], a[1], scale, false);
+      out[i] = cvt2_f32<F>(w, a[2], a[3], scale, true);
+    }
   }
 }
 

@@ -65,7 +65,7 @@ __device__ __forceinline__ void load_chunk(Chunk<SRC_BF16>& c, const void* line,
 // consecutive blocks, so its 64 scale bytes form one contiguous run.  Blocks are
 // numbered g = row * nb + b (FLAT problems are one dense run: row 0, b = g).  One block
 // per thread and a large grid keep enough loads in flight to stream HBM.
-template <int SRC_BF16, int F, bool FLAT, bool VEC>
+template <int SRC_BF16, int F, bool FLAT, bool VEC, int R>
 __global__ __launch_bounds__(kThreads) void k_quant_rows(const void* __restrict__ src, int64_t ld_src, int64_t K,
                                                         int64_t nb, int64_t nblocks, uint8_t* __restrict__ codes,
                                                         int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales) {
@@ -85,10 +85,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(const void* __restrict_
       const uint32_t a = chunk_abs_max<SRC_BF16>(c[q]);
       amax = amax > a ? amax : a;
     }
-    const uint32_t sb = scale_byte_from_amax<F>(amax);
+    const uint32_t sb = scale_byte_rule<F, R>(amax);
     uint32_t d[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) encode_chunk<SRC_BF16, F>(c[q], sb, d[2 * q], d[2 * q + 1]);
+    for (int q = 0; q < 4; ++q) encode_chunk<SRC_BF16, F, R>(c[q], sb, d[2 * q], d[2 * q + 1]);
     uint4* out = reinterpret_cast<uint4*>(codes + row * ld_codes + 32 * b);
     out[0] = make_uint4(d[0], d[1], d[2], d[3]);
     out[1] = make_uint4(d[4], d[5], d[6], d[7]);
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(const void* __restrict_
 constexpr int kColTileRows = 128;
 constexpr int kColTileCols = 64;
 
-template <int SRC_BF16, int F, bool VEC>
+template <int SRC_BF16, int F, bool VEC, int R>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(const void* __restrict__ src, int64_t rows, int64_t cols,
                                                         int64_t ld_src, int64_t nb, uint8_t* __restrict__ codes,
                                                         int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales) {
@@ -153,27 +153,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols(const void* __restrict_
         const uint32_t a = x & 0x7FFFFFFFu;
         amax = amax > a ? amax : a;
       }
-      const uint32_t sb = scale_byte_from_amax<F>(amax);
+      const uint32_t sb = scale_byte_rule<F, R>(amax);
       uint32_t out[8];
-      if (sb == 255u) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = 0x7F7F7F7Fu;
-      } else if (sb == 0u) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w |= encode_rne_sat<F>(__uint_as_float(v[4 * i + j]) * 0x1p127f) << (8 * j);
-          out[i] = w;
-        }
-      } else {
-        const float scale = __uint_as_float(sb << 23);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t w = cvt2_f32<F>(0u, v[4 * i], v[4 * i + 1], scale, false);
-          out[i] = cvt2_f32<F>(w, v[4 * i + 2], v[4 * i + 3], scale, true);
-        }
-      }
+      encode_block32<F, R>(v, sb, out);
       uint4* dst = reinterpret_cast<uint4*>(codes + col * ld_codes + 32 * b);
       dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
       dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
@@ -253,25 +235,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(const void* __restrict_
       }
       const uint32_t sb = scale_byte_from_amax<F>(amax);
       uint32_t out[8];
-      if (sb == 255u) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) out[i] = 0x7F7F7F7Fu;
-      } else if (sb == 0u) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) w |= encode_rne_sat<F>(__uint_as_float(v[4 * i + j]) * 0x1p127f) << (8 * j);
-          out[i] = w;
-        }
-      } else {
-        const float scale = __uint_as_float(sb << 23);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t w = cvt2_f32<F>(0u, v[4 * i], v[4 * i + 1], scale, false);
-          out[i] = cvt2_f32<F>(w, v[4 * i + 2], v[4 * i + 3], scale, true);
-        }
-      }
+      encode_block32<F>(v, sb, out);
       uint4* dst = reinterpret_cast<uint4*>(ccodes + col * ld_cc + 32 * b);
       dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
       dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
@@ -552,7 +516,7 @@ int device_cu_count() {
   return cache[dev];
 }
 
-template <int SRC_BF16, int F>
+template <int SRC_BF16, int F, int R>
 static hipError_t quant_rows_t(const void* src, int64_t rows, int64_t K, int64_t ld_src, uint8_t* codes,
                                int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool flat, bool vec,
                                hipStream_t stream) {
@@ -562,29 +526,38 @@ static hipError_t quant_rows_t(const void* src, int64_t rows, int64_t K, int64_t
   const int64_t cap = (int64_t)device_cu_count() * 256;   // beyond this, threads loop
   const int grid = (int)(wg_needed < cap ? wg_needed : cap);
   if (flat && vec)
-    hipLaunchKernelGGL((k_quant_rows<SRC_BF16, F, true, true>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src, K,
+    hipLaunchKernelGGL((k_quant_rows<SRC_BF16, F, true, true, R>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src, K,
                        nb, nblocks, codes, ld_codes, scales, ld_scales);
   else if (vec)
-    hipLaunchKernelGGL((k_quant_rows<SRC_BF16, F, false, true>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src, K,
+    hipLaunchKernelGGL((k_quant_rows<SRC_BF16, F, false, true, R>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src, K,
                        nb, nblocks, codes, ld_codes, scales, ld_scales);
   else
-    hipLaunchKernelGGL((k_quant_rows<SRC_BF16, F, false, false>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src,
+    hipLaunchKernelGGL((k_quant_rows<SRC_BF16, F, false, false, R>), dim3(grid), dim3(kThreads), 0, stream, src, ld_src,
                        K, nb, nblocks, codes, ld_codes, scales, ld_scales);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_rows(const void* src, int src_bf16, int64_t rows, int64_t K, int64_t ld_src, int fmt,
-                             uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool flat,
-                             bool vec, hipStream_t stream) {
+template <int R>
+static hipError_t quant_rows_r(const void* src, int src_bf16, int64_t rows, int64_t K, int64_t ld_src, int fmt,
+                               uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool flat,
+                               bool vec, hipStream_t stream) {
   if (src_bf16) {
-    if (fmt == kE4M3) return quant_rows_t<1, kE4M3>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
-    return quant_rows_t<1, kE5M2>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
+    if (fmt == kE4M3) return quant_rows_t<1, kE4M3, R>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
+    return quant_rows_t<1, kE5M2, R>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
   }
-  if (fmt == kE4M3) return quant_rows_t<0, kE4M3>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
-  return quant_rows_t<0, kE5M2>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
+  if (fmt == kE4M3) return quant_rows_t<0, kE4M3, R>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
+  return quant_rows_t<0, kE5M2, R>(src, rows, K, ld_src, codes, ld_codes, scales, ld_scales, flat, vec, stream);
 }
 
-template <int SRC_BF16, int F>
+hipError_t launch_quant_rows(const void* src, int src_bf16, int64_t rows, int64_t K, int64_t ld_src, int fmt,
+                             int rule, uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                             bool flat, bool vec, hipStream_t stream) {
+  if (rule == kRuleOcp)
+    return quant_rows_r<kRuleOcp>(src, src_bf16, rows, K, ld_src, fmt, codes, ld_codes, scales, ld_scales, flat, vec, stream);
+  return quant_rows_r<kRuleCeil>(src, src_bf16, rows, K, ld_src, fmt, codes, ld_codes, scales, ld_scales, flat, vec, stream);
+}
+
+template <int SRC_BF16, int F, int R>
 static hipError_t quant_cols_t(const void* src, int64_t rows, int64_t cols, int64_t ld_src, uint8_t* codes,
                                int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec, hipStream_t stream) {
   const int64_t nb = (rows + 31) / 32;
@@ -593,23 +566,32 @@ static hipError_t quant_cols_t(const void* src, int64_t rows, int64_t cols, int6
   if (gy > 65535) gy = 65535;
   if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (vec)
-    hipLaunchKernelGGL((k_quant_cols<SRC_BF16, F, true>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((k_quant_cols<SRC_BF16, F, true, R>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream,
                        src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales);
   else
-    hipLaunchKernelGGL((k_quant_cols<SRC_BF16, F, false>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((k_quant_cols<SRC_BF16, F, false, R>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream,
                        src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_cols(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, int fmt,
-                             uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec,
-                             hipStream_t stream) {
+template <int R>
+static hipError_t quant_cols_r(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, int fmt,
+                               uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec,
+                               hipStream_t stream) {
   if (src_bf16) {
-    if (fmt == kE4M3) return quant_cols_t<1, kE4M3>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
-    return quant_cols_t<1, kE5M2>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+    if (fmt == kE4M3) return quant_cols_t<1, kE4M3, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+    return quant_cols_t<1, kE5M2, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
   }
-  if (fmt == kE4M3) return quant_cols_t<0, kE4M3>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
-  return quant_cols_t<0, kE5M2>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+  if (fmt == kE4M3) return quant_cols_t<0, kE4M3, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+  return quant_cols_t<0, kE5M2, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+}
+
+hipError_t launch_quant_cols(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, int fmt,
+                             int rule, uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec,
+                             hipStream_t stream) {
+  if (rule == kRuleOcp)
+    return quant_cols_r<kRuleOcp>(src, src_bf16, rows, cols, ld_src, fmt, codes, ld_codes, scales, ld_scales, vec, stream);
+  return quant_cols_r<kRuleCeil>(src, src_bf16, rows, cols, ld_src, fmt, codes, ld_codes, scales, ld_scales, vec, stream);
 }
 
 template <int SRC_BF16, int F>

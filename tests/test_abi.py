@@ -18,7 +18,7 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert {"mxq_quantize", "mxq_quantize_dual", "mxq_quantize_sr", "mxq_quantize_scaled", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex",
+    assert {"mxq_quantize", "mxq_quantize_rule", "mxq_quantize_dual", "mxq_quantize_sr", "mxq_quantize_scaled", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex",
             "mxq_status_string", "mxq_version"} <= set(declared_symbols())
 
 
@@ -68,6 +68,25 @@ def test_quantize_validation():
     # empty problems succeed without touching pointers
     assert q(rows=0, src=None, codes=None, scales=None) == 0
     assert q(cols=0, src=None, codes=None, scales=None) == 0
+
+
+def test_quantize_rule_validation():
+    def qr(rule, **kw):
+        a = dict(src=FAKE, src_type=mxq.MXQ_BF16, rows=4, cols=64, ld_src=64, axis=mxq.MXQ_ROWWISE,
+                 elem=mxq.MXQ_E4M3, codes=FAKE, ld_codes=64, scales=FAKE, ld_scales=2)
+        a.update(kw)
+        return mxq.mxq_quantize_rule(a["src"], a["src_type"], a["rows"], a["cols"], a["ld_src"], a["axis"],
+                                     a["elem"], rule, a["codes"], a["ld_codes"], a["scales"], a["ld_scales"], None)
+    assert qr(2) == -6
+    assert qr(-1) == -6
+    for rule in (mxq.MXQ_SCALE_CEIL, mxq.MXQ_SCALE_OCP):
+        assert qr(rule, src_type=mxq.MXQ_E4M3) == -5
+        assert qr(rule, axis=7) == -6
+        assert qr(rule, rows=-1) == -2
+        assert qr(rule, codes=None) == -1
+        assert qr(rule, ld_codes=48) == -3
+        assert qr(rule, codes=FAKE + 8) == -4
+        assert qr(rule, rows=0, src=None, codes=None, scales=None) == 0
 
 
 def test_quantize_sr_validation():

@@ -32,6 +32,8 @@ def test_quantize_rejections():
     raises(lambda: mxq.quantize(bf(4, 64), codes=torch.zeros(4, 64, dtype=torch.int8)), "codes must be torch.uint8")
     raises(lambda: mxq.quantize(bf(40, 4), axis="col", codes=u8(4, 32)), "needs at least 64")
     raises(lambda: mxq.quantize(bf(4, 64)), "CUDA")
+    raises(lambda: mxq.quantize(bf(4, 64), rule="floor"), "rule")
+    raises(lambda: mxq.quantize(bf(4, 64), rule="ocp"), "CUDA")
 
 
 def test_other_quantizers_reject_host_tensors_and_bad_shapes():
