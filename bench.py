@@ -16,10 +16,14 @@ elements is reported against the HBM peak.  The CPU oracle is timed on a bounded
 of the same step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-calibration]
-                       [--headline-only]
+                       [--headline-only] [--only KERNEL]
 
 --headline-only times the step alone (no components, no CPU leg): the short run that
 counter passes profile.
+
+--only quantize_2p28 | quantize_2p28_colwise | quantize_2p28_dual runs that one quantize
+launch on the [16384][16384] bf16 input, W untimed then K timed, and prints its time and
+GB/s (the short run that the quantize kernels' counter passes profile).
 
 --copy-calibration adds a plain elementwise copy of a known size (256 MiB read, 256 MiB
 written) after the measurement, so that one hardware-counter run sees both the GEMM and a
@@ -53,7 +57,13 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     p.add_argument("--copy-calibration", action="store_true", help="also run a copy of known size (counter runs)")
     p.add_argument("--headline-only", action="store_true", help="time the step only (counter runs)")
+    p.add_argument("--only", choices=sorted(ONLY_KERNELS), default=None,
+                   help="time one standalone quantize kernel on the 2^28 input alone (counter runs)")
     return p.parse_args()
+
+
+# --only: one quantize entry point on the [16384][16384] bf16 input, E4M3
+ONLY_KERNELS = {"quantize_2p28": "rowwise", "quantize_2p28_colwise": "colwise", "quantize_2p28_dual": "dual"}
 
 
 GEMM_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_03_amd", "csrc", "gemm.hip")
@@ -95,6 +105,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     mxq.lib()
+    if args.only:
+        only_quantize(args, torch, mxq, wl, dev)
+        return
 
     d = wl.workload2()
     M, K, N = d["M"], d["K"], d["N"]
@@ -421,6 +434,53 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(d, xc, xs, wc, ws, M, N, K, args.cpu_seconds)
     print(json.dumps(out))
+
+
+def only_quantize(args, torch, mxq, wl, dev):
+    """One quantize entry point alone on the 2^28-element input: bytes moved per launch are
+    2 B read + (1 + 1/32) B written per element and orientation."""
+    import ctypes
+    L = mxq.lib()
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    qx = wl.workload_q()["x"].to(dev)
+    R, C = qx.shape
+    kind = ONLY_KERNELS[args.only]
+    rc = torch.empty((R, C), dtype=torch.uint8, device=dev)
+    rs = torch.empty((R, C // 32), dtype=torch.uint8, device=dev)
+    if kind == "dual":
+        cc = torch.empty((C, R), dtype=torch.uint8, device=dev)
+        cs = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
+        a = (qx.data_ptr(), mxq.MXQ_BF16, R, C, qx.stride(0), mxq.MXQ_E4M3, rc.data_ptr(), rc.stride(0),
+             rs.data_ptr(), rs.stride(0), cc.data_ptr(), cc.stride(0), cs.data_ptr(), cs.stride(0), sh)
+        call = lambda: L.mxq_quantize_dual(*a)  # noqa: E731
+        nbytes = R * C * (2 + 2 * (1 + 1 / 32))
+    else:
+        axis = mxq.MXQ_ROWWISE if kind == "rowwise" else mxq.MXQ_COLWISE
+        if kind == "colwise":
+            rc = rc.view(C, R)
+            rs = torch.empty((C, R // 32), dtype=torch.uint8, device=dev)
+        a = (qx.data_ptr(), mxq.MXQ_BF16, R, C, qx.stride(0), axis, mxq.MXQ_E4M3, rc.data_ptr(), rc.stride(0),
+             rs.data_ptr(), rs.stride(0), sh)
+        call = lambda: L.mxq_quantize(*a)  # noqa: E731
+        nbytes = R * C * (2 + 1 + 1 / 32)
+    st = call()
+    if st != 0:
+        raise RuntimeError("%s failed: %s" % (args.only, mxq.mxq_status_string(st)))
+    for _ in range(args.warmup):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    print(json.dumps({"kernel": args.only, "workload": "[16384][16384] bf16, E4M3", "steps": args.steps,
+                      "ms": round(ms, 5), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}))
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
 
 
 def copy_calibration(torch, dev):

@@ -75,7 +75,7 @@ int mxq_quantize_rule(const void* src, int src_type, int64_t rows, int64_t cols,
                                              codes, ld_codes, scales, ld_scales, flat, vec, st));
   }
   return hip_status(mxq::launch_quant_cols(src, src_type == MXQ_BF16, rows, cols, ld_src, to_fmt(elem), to_rule(rule),
-                                           codes, ld_codes, scales, ld_scales, src16, st));
+                                           codes, ld_codes, scales, ld_scales, st));
 }
 
 int mxq_quantize_sr(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int axis, int elem,

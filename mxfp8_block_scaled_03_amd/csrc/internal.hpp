@@ -20,7 +20,7 @@ hipError_t launch_quant_rows(const void* src, int src_bf16, int64_t rows, int64_
 // scales stored [cols][ld].
 hipError_t launch_quant_cols(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src,
                              int fmt, int rule, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
-                             int64_t ld_scales, bool vec, hipStream_t stream);
+                             int64_t ld_scales, hipStream_t stream);
 
 // Both orientations in one pass: rowwise codes [rows][ld_rc] (K = cols) and columnwise
 // codes [cols][ld_cc] (K = rows), with their scales.

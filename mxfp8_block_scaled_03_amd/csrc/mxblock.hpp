@@ -180,6 +180,44 @@ __device__ __forceinline__ uint32_t chunk_abs_max(const Chunk<SRC_BF16>& c) {
   }
 }
 
+// Codes of one column of 32 bf16 values held in the low (hi = false) or high halves of
+// 32 dwords w[i] (row i of the block; the other half belongs to the neighbouring column):
+// for a normal scale byte, pairs of rows are gathered into one packed bf16 dword
+// (v_perm_b32) and converted two at a time; scale bytes 0 and 255 take encode_block32.
+template <int F, int R = kRuleCeil>
+__device__ __forceinline__ void encode_block32_bf16_half(const uint32_t w[32], bool hi, uint32_t sb, uint32_t out[8]) {
+  if (sb == 255u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = 0x7F7F7F7Fu;
+    return;
+  }
+  if (sb == 0u) {                                  // value by value, as encode_block32
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t v = hi ? (w[4 * i + j] & 0xFFFF0000u) : (w[4 * i + j] << 16);
+        c |= encode_rne_sat<F>(__uint_as_float(v) * 0x1p127f) << (8 * j);
+      }
+      out[i] = c;
+    }
+    return;
+  }
+  const float scale = __uint_as_float(sb << 23);
+  const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t p0 = __builtin_amdgcn_perm(w[4 * j + 1], w[4 * j], sel);
+    uint32_t p1 = __builtin_amdgcn_perm(w[4 * j + 3], w[4 * j + 2], sel);
+    if (R == kRuleOcp) {
+      p0 = clamp_pk_bf16<F>(p0, sb);
+      p1 = clamp_pk_bf16<F>(p1, sb);
+    }
+    out[j] = cvt2_bf16<F>(cvt2_bf16<F>(0u, p0, scale, false), p1, scale, true);
+  }
+}
+
 // ---- stochastic rounding ("Rounding: RNE versus stochastic rounding": between the
 //      neighbouring representable values l <= |a| < u, round up with probability
 //      (|a| - l) / (u - l); representable values stay)

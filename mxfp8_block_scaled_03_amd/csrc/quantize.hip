@@ -96,74 +96,271 @@ __global__ __launch_bounds__(kThreads) void k_quant_rows(const void* __restrict_
   }
 }
 
-// Columnwise: a workgroup stages a tile of 128 rows (4 blocks of K) x 64 columns in LDS
-// (row pitch padded by one dword, which spreads the column reads over the banks), then
-// thread t handles column t / 4, block t % 4: it reduces and encodes that block's 32
-// values and writes its 32 codes, so the 4 threads of a column write one contiguous
-// 128-byte run of the K-contiguous transposed output.
-constexpr int kColTileRows = 128;
-constexpr int kColTileCols = 64;
+// Columnwise, straight from HBM: the path for sources whose rows are not whole, aligned
+// 16-byte pieces (k_quant_cols_lds below takes the rest).  A wave's task is 512 rows (16
+// blocks, taken as 4 sub-tiles of 128 rows) of 64 consecutive columns, one column per
+// lane: every load of
+// the wave reads one contiguous row segment (128 bytes of bf16, 256 of fp32).  The lane
+// reduces and encodes its column a block at a time, keeps the sub-tile's 128 codes in
+// registers and writes them as one burst of eight 16-byte stores; the task's 16 scale
+// bytes go out as one 16-byte store at the end.  No LDS and no barrier.
+// Counter evidence behind the shape (2^28 bf16, WRITE_SIZE against the 264 MiB the
+// kernel writes): a column's 128-byte line of codes written in 32-byte pieces, whether by
+// four waves or by one wave a block apart, gave 380-415 MiB; scale bytes written 4 at a
+// time from tiles on different XCDs gave 340 MiB with whole code lines; whole code lines
+// and 16-byte scale pieces whose 128-byte line is completed on one XCD give 286 MiB.
+// The 4 waves of a workgroup take 4 adjacent column strips of one 512-row group;
+// workgroup tasks are numbered strip-major (the groups of one strip consecutive, so the 8
+// tasks that share a column's 128-byte scale line run together on one XCD) and dealt to
+// the XCDs in contiguous chunks (workgroup g runs on XCD g % 8).
+constexpr int kColGroupRows = 512;   // rows of a task: 16 blocks
+constexpr int kXcds = 8;
+constexpr int kColStrip = 64;        // columns per wave task
 
-template <int SRC_BF16, int F, bool VEC, int R>
+// gx column strips and ng = ceil(rows / 512) row groups; workgroup tasks (4 strips x 1
+// group) number wg_total = ceil(gx / 4) * ng; XCD g % 8 owns tasks
+// [xcd * per_xcd, (xcd + 1) * per_xcd) and its workgroups stride through them by
+// slots = gridDim / 8.
+struct ColTiles {
+  int64_t wg_total, per_xcd, gx, ng;
+};
+
+// BUF: the task's rows are read through a buffer descriptor based at the task's first
+// element of row r0 whose range ends at the last valid element, so rows past the matrix
+// read as zero (the zero padding) and each load is one scalar row offset plus the lane's
+// byte offset; it needs 512 rows within 2^31 bytes, otherwise element loads with explicit
+// bounds.  A bf16 value lands in the low half of its dword.  vsc: scales and ld_scales
+// are 16-byte aligned, so a whole task's 16 scale bytes are one store.
+template <int SRC_BF16, int F, bool BUF, int R>
 __global__ __launch_bounds__(kThreads) void k_quant_cols(const void* __restrict__ src, int64_t rows, int64_t cols,
                                                         int64_t ld_src, int64_t nb, uint8_t* __restrict__ codes,
-                                                        int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales) {
-  typedef typename std::conditional<SRC_BF16, uint16_t, uint32_t>::type E;
-  constexpr int PW = kColTileCols * (int)sizeof(E) / 4 + 1;      // row pitch in dwords
-  __shared__ uint32_t tile[kColTileRows * PW];
-  const int tid = threadIdx.x;
-  const int64_t c0 = (int64_t)blockIdx.x * kColTileCols;
-  const E* s = reinterpret_cast<const E*>(src);
-  for (int64_t ty = blockIdx.y; ty * kColTileRows < rows; ty += gridDim.y) {
-    const int64_t r0 = ty * kColTileRows;
-    // stage: 16-byte pieces of each tile row, written to LDS as 4 dwords
-    constexpr int EPV = 16 / sizeof(E);                 // elements per 16-byte piece
-    constexpr int PPR = kColTileCols / EPV;             // pieces per tile row
-    for (int p = tid; p < kColTileRows * PPR; p += kThreads) {
-      const int tr = p / PPR, tc = (p % PPR) * EPV;
-      const int64_t r = r0 + tr, cc = c0 + tc;
-      uint32_t* dst = &tile[tr * PW + tc * (int)sizeof(E) / 4];
-      if (VEC && r < rows && cc + EPV <= cols) {
-        const uint4 v = *reinterpret_cast<const uint4*>(s + r * ld_src + cc);
-        dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
-      } else {
-        E e[EPV];
+                                                        int64_t ld_codes, uint8_t* __restrict__ scales,
+                                                        int64_t ld_scales, ColTiles tiles, int vsc) {
+  constexpr int ES = SRC_BF16 ? 2 : 4;
+  const int64_t xcd = blockIdx.x % kXcds;
+  const int64_t slots = gridDim.x / kXcds;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // the wave index: scalar
+  for (int64_t s = blockIdx.x / kXcds; s < tiles.per_xcd; s += slots) {
+    const int64_t t = xcd * tiles.per_xcd + s;
+    if (t >= tiles.wg_total) break;
+    const int64_t xw = t / tiles.ng, g = t - xw * tiles.ng;
+    const int64_t x = 4 * xw + wv;
+    if (x >= tiles.gx) continue;                   // uniform over the wave
+    const int64_t c0 = x * kColStrip, col = c0 + lane;
+    const bool live = col < cols;
+    const int64_t b0 = 16 * g, r0 = 32 * b0;
+    const int nblk = nb - b0 < 16 ? (int)(nb - b0) : 16;          // uniform
+    const bool full = vsc && nblk == 16;
+    // (unused without BUF: a descriptor of range 0)
+    const int64_t nvalid = rows - r0 < kColGroupRows ? rows - r0 : kColGroupRows;
+    const char* base = reinterpret_cast<const char*>(src) + (BUF ? (r0 * ld_src + c0) * ES : 0);
+    const uint32_t range = BUF ? (uint32_t)(((nvalid - 1) * ld_src + (cols - c0)) * ES) : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)range, 0x00020000);
+    const int row_bytes = BUF ? (int)(ld_src * ES) : 0;
+    uint32_t q[4];                                 // scale bytes of the task, block k in byte k
+    for (int st = 0; st < 4; ++st) {
+      const int kb0 = 4 * st;
+      if (kb0 >= nblk) break;                      // uniform
+      const int nsub = nblk - kb0 < 4 ? nblk - kb0 : 4;
+      uint32_t c[32];                              // codes of the sub-tile's (up to) 4 blocks
+      uint32_t sw = 0;
 #pragma unroll
-        for (int i = 0; i < EPV; ++i) e[i] = (r < rows && cc + i < cols) ? s[r * ld_src + cc + i] : (E)0;
+      for (int j = 0; j < 4; ++j) {
+        if (j >= nsub) break;                      // uniform
+        const int k = kb0 + j;
+        uint32_t w[32];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          if (SRC_BF16) dst[w] = (uint32_t)e[2 * w] | ((uint32_t)e[2 * w + 1] << 16);
-          else dst[w] = (uint32_t)e[w];
+        for (int i = 0; i < 32; ++i) {
+          if (BUF) {
+            w[i] = SRC_BF16 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, 2 * lane, (32 * k + i) * row_bytes, 0)
+                            : __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane, (32 * k + i) * row_bytes, 0);
+          } else {
+            const int64_t r = r0 + 32 * k + i;
+            w[i] = 0u;
+            if (live && r < rows)
+              w[i] = SRC_BF16 ? (uint32_t)reinterpret_cast<const uint16_t*>(src)[r * ld_src + col]
+                              : reinterpret_cast<const uint32_t*>(src)[r * ld_src + col];
+          }
         }
-      }
-    }
-    __syncthreads();
-    const int c = tid >> 2, kb = tid & 3;
-    const int64_t col = c0 + c, b = r0 / 32 + kb;
-    if (col < cols && b < nb) {
-      uint32_t amax = 0;
-      uint32_t v[32];
+        uint32_t sb;
+        if (SRC_BF16) {
+          uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int row = 32 * kb + i;
-        uint32_t x;
-        if (SRC_BF16) x = (uint32_t)reinterpret_cast<const uint16_t*>(tile)[row * PW * 2 + c] << 16;
-        else x = tile[row * PW + c];
-        v[i] = x;
-        const uint32_t a = x & 0x7FFFFFFFu;
-        amax = amax > a ? amax : a;
+          for (int i = 0; i < 32; ++i) m = pk_abs_max_bf16(m, w[i]);
+          sb = scale_byte_rule<F, R>(m << 16);
+          encode_block32_bf16_half<F, R>(w, false, sb, &c[8 * j]);
+        } else {
+          uint32_t amax = 0;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const uint32_t a = w[i] & 0x7FFFFFFFu;
+            amax = amax > a ? amax : a;
+          }
+          sb = scale_byte_rule<F, R>(amax);
+          encode_block32<F, R>(w, sb, &c[8 * j]);
+        }
+        sw |= sb << (8 * j);
       }
-      const uint32_t sb = scale_byte_rule<F, R>(amax);
-      uint32_t out[8];
-      encode_block32<F, R>(v, sb, out);
-      uint4* dst = reinterpret_cast<uint4*>(codes + col * ld_codes + 32 * b);
-      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-      scales[col * ld_scales + b] = (uint8_t)sb;
+      q[st] = sw;
+      if (!live) continue;
+      uint4* dst = reinterpret_cast<uint4*>(codes + col * ld_codes + 32 * (b0 + kb0));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j >= nsub) break;
+        dst[2 * j] = make_uint4(c[8 * j], c[8 * j + 1], c[8 * j + 2], c[8 * j + 3]);
+        dst[2 * j + 1] = make_uint4(c[8 * j + 4], c[8 * j + 5], c[8 * j + 6], c[8 * j + 7]);
+      }
+      if (!full)
+        for (int j = 0; j < nsub; ++j) scales[col * ld_scales + b0 + kb0 + j] = (uint8_t)(sw >> (8 * j));
     }
-    __syncthreads();
+    if (full && live) *reinterpret_cast<uint4*>(scales + col * ld_scales + b0) = make_uint4(q[0], q[1], q[2], q[3]);
   }
 }
+
+// Columnwise through LDS, for rows of whole 16-byte pieces (bf16: cols % 8 == 0,
+// fp32: cols % 4 == 0; 16-byte aligned src and row pitch).  A workgroup takes one tile of
+// 128 rows (4 blocks) x 64 columns (16 KB of bf16, 32 KB of fp32), so a launch has many
+// small independent workgroups.  The tile moves from HBM with 16-byte loads (a wave load
+// covers whole 128/256-byte row segments), is written to LDS row-major and read back down
+// the columns: lane 4c + kb of wave w takes column 16w + c, block kb.  Row r is stored
+// with its dword index xor SWZ * ((r >> 5) & 3) (SWZ = the dwords of 8 columns), so the
+// four blocks read by a half-wave fall on different banks.  The four lanes of a column
+// write its 128-byte line of codes in the same pair of store instructions.
+// Earlier shapes of this kernel, on 2^28 bf16: the same tile without the swizzle (4-way
+// LDS bank conflicts, 20% of the cycles) took 204 us; a direct kernel with one column per
+// lane and one 128/256-byte row segment per load took 240 us (its loads touch one cache
+// line each: the texture address unit stalled on the L1 3x as often as the rowwise
+// kernel's at the same L2 latency); a persistent kernel with 128 x 128 tiles, 3
+// workgroups per CU and a register prefetch took 221 us.
+// Tile t of a gy x gx grid of tiles, in groups of GH x GW tiles: x fastest inside a
+// group, groups in row-band order, narrower or shorter groups at the right and bottom
+// edges (a bijection of [0, gx * gy)).  Workgroup g takes tile (g % 8) * ceil(n / 8) + g / 8,
+// so each XCD runs a contiguous run of groups.  For the transposing kernels the group
+// shape trades the two halves of the traffic: the workgroups in flight on an XCD read
+// GW adjacent 128-byte pieces of each source row (long DRAM runs) and write the
+// transposed codes at GH different row offsets (spread over the memory channels; a
+// whole row band at one offset, the plain row-major order, writes every line at the same
+// offset within its 16 KB row).  Measured on 2^28 bf16 columnwise: row-major order
+// 198 us; 16 x 16 groups 169 us; 8 x 32 159 us; 8 x 64 156 us; 2 x 128 175 us;
+// 64 x 4 188 us.
+template <int64_t GH, int64_t GW>
+__device__ __forceinline__ void grouped_tile(int64_t t, int64_t gx, int64_t gy, int64_t& y, int64_t& x) {
+  const int64_t band = t / (GH * gx), rem = t - band * GH * gx;
+  const int64_t hb = gy - GH * band < GH ? gy - GH * band : GH;
+  const int64_t grp = rem / (GW * hb), r2 = rem - grp * GW * hb;
+  const int64_t wdt = gx - GW * grp < GW ? gx - GW * grp : GW;
+  y = GH * band + r2 / wdt;
+  x = GW * grp + r2 % wdt;
+}
+
+constexpr int kColGroupH = 8, kColGroupW = 64;    // columnwise tile group: rows x columns of tiles
+
+template <int SRC_BF16>
+struct CtGeom {
+  static constexpr int ES = SRC_BF16 ? 2 : 4;
+  static constexpr int TC = 64;                     // tile columns (4 lanes each)
+  static constexpr int RW = TC * ES / 4;            // dwords per tile row: 32 / 64
+  static constexpr int PPR = TC * ES / 16;          // 16-byte pieces per row: 8 / 16
+  static constexpr int NP = 128 * PPR / kThreads;   // pieces per thread: 4 / 8
+  static constexpr int CPW = TC / 4;                // columns per wave: 16
+  static constexpr int SWZ = 2 * ES;                // dwords of a half-wave's 8 columns
+};
+
+template <int SRC_BF16, int F, int R>
+__global__ __launch_bounds__(kThreads) void k_quant_cols_lds(const void* __restrict__ src, int64_t rows,
+                                                            int64_t cols, int64_t ld_src, int64_t nb,
+                                                            uint8_t* __restrict__ codes, int64_t ld_codes,
+                                                            uint8_t* __restrict__ scales, int64_t ld_scales,
+                                                            int64_t gx, int64_t ntiles, int64_t per_xcd) {
+  typedef CtGeom<SRC_BF16> G;
+  __shared__ __align__(16) uint32_t ctile[128 * G::RW];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int64_t t = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (t >= ntiles) return;                           // the whole workgroup, before any barrier
+  int64_t y, x;
+  grouped_tile<kColGroupH, kColGroupW>(t, gx, ntiles / gx, y, x);
+  const int64_t c0 = x * G::TC, r0 = 128 * y;
+  const int64_t nvalid = rows - r0 < 128 ? rows - r0 : 128;
+  const char* base = reinterpret_cast<const char*>(src) + (r0 * ld_src + c0) * G::ES;
+  const uint32_t range = (uint32_t)(((nvalid - 1) * ld_src + (cols - c0)) * G::ES);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)range, 0x00020000);
+  const int row_bytes = (int)(ld_src * G::ES);
+  uint4 v[G::NP];
+#pragma unroll
+  for (int q = 0; q < G::NP; ++q) {
+    const int p = tid + kThreads * q;
+    const auto d = __builtin_amdgcn_raw_buffer_load_b128(rs, (p / G::PPR) * row_bytes + (p % G::PPR) * 16, 0, 0);
+    v[q] = make_uint4((uint32_t)d[0], (uint32_t)d[1], (uint32_t)d[2], (uint32_t)d[3]);
+  }
+#pragma unroll
+  for (int q = 0; q < G::NP; ++q) {
+    const int p = tid + kThreads * q;
+    const int row = p / G::PPR;
+    const int d = ((p % G::PPR) * 4) ^ (G::SWZ * ((row >> 5) & 3));
+    *reinterpret_cast<uint4*>(&ctile[row * G::RW + d]) = v[q];
+  }
+  __syncthreads();
+  const int kb = lane & 3;
+  const int cl = G::CPW * wv + (lane >> 2);          // column within the tile
+  const int64_t col = c0 + cl, b = 4 * y + kb;
+  if (col >= cols || b >= nb) return;                // no barrier follows
+  uint32_t w[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int row = 32 * kb + i;
+    const int sw = G::SWZ * kb;                      // (row >> 5) & 3 == kb
+    if (SRC_BF16) {
+      const int d = (cl >> 1) ^ sw;
+      w[i] = (uint32_t)reinterpret_cast<const uint16_t*>(ctile)[2 * (row * G::RW + d) + (cl & 1)];
+    } else {
+      w[i] = ctile[row * G::RW + (cl ^ sw)];
+    }
+  }
+  uint32_t c[8], sb;
+  if (SRC_BF16) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) m = pk_abs_max_bf16(m, w[i]);
+    sb = scale_byte_rule<F, R>(m << 16);
+    encode_block32_bf16_half<F, R>(w, false, sb, c);
+  } else {
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t a = w[i] & 0x7FFFFFFFu;
+      amax = amax > a ? amax : a;
+    }
+    sb = scale_byte_rule<F, R>(amax);
+    encode_block32<F, R>(w, sb, c);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes + col * ld_codes + 32 * b);
+  dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+  dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+  scales[col * ld_scales + b] = (uint8_t)sb;
+}
+
+// Column tasks of a [rows][cols] problem and the launch size: 8 * ceil(tasks / 8)
+// workgroups, capped so that each XCD's workgroups loop (every wave reaches the end of
+// the loop: the trip count depends only on the workgroup index and the task count).
+static ColTiles col_tiles(int64_t rows, int64_t cols, int64_t* grid) {
+  ColTiles t;
+  t.gx = (cols + kColStrip - 1) / kColStrip;
+  t.ng = (rows + kColGroupRows - 1) / kColGroupRows;
+  t.wg_total = (t.gx + 3) / 4 * t.ng;
+  t.per_xcd = (t.wg_total + kXcds - 1) / kXcds;
+  const int64_t cap = (int64_t)device_cu_count() * 8 / kXcds;    // workgroups per XCD
+  *grid = kXcds * (t.per_xcd < cap ? t.per_xcd : cap);
+  return t;
+}
+
+// The LDS-staged column kernels (dual, stochastic rounding, caller-owned scales) take
+// tiles of 128 rows x 64 columns.
+constexpr int kColTileRows = 128;
+constexpr int kColTileCols = 64;
 
 
 // Both orientations from one read ("Microscaling: the two-row experiment", last
@@ -244,6 +441,119 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual(const void* __restrict_
     __syncthreads();
   }
 }
+// Both orientations through LDS, for rows of whole 16-byte pieces (the conditions of
+// k_quant_cols_lds).  A workgroup takes one tile of 128 rows x 128 columns (32 KB of
+// bf16, 64 KB of fp32): thread t's q-th chunk (8 values: one 16-byte load of bf16, two of
+// fp32) is row p / 16, chunk p % 16 with p = t + 256 q, so the four lanes of a quad hold
+// one 32-value row block (reduced with DPP) and the 16 lanes of a row write its 128-byte
+// line of rowwise codes in one store instruction.  Columns past cols read as zero (they
+// are the rowwise zero padding).  The tile goes to LDS in the swizzled layout of
+// k_quant_cols_lds and is read back down the columns in two passes of 64 columns: lane
+// 4c + kb of wave w takes column 64u + 16w + c, block kb, and the four lanes of a column
+// write its 128-byte line of columnwise codes together.  With 128 x 64 tiles, the rowwise
+// codes went out as 64-byte half-lines from two workgroups and the counters showed 17%
+// more HBM write bytes than the kernel writes.
+constexpr int kDualGroupH = 8, kDualGroupW = 32;  // dual tile group (tiles of 128 columns)
+
+template <int SRC_BF16, int F>
+__global__ __launch_bounds__(kThreads) void k_quant_dual_lds(const void* __restrict__ src, int64_t rows, int64_t cols,
+                                                            int64_t ld_src, uint8_t* __restrict__ rcodes, int64_t ld_rc,
+                                                            uint8_t* __restrict__ rscales, int64_t ld_rs,
+                                                            uint8_t* __restrict__ ccodes, int64_t ld_cc,
+                                                            uint8_t* __restrict__ cscales, int64_t ld_cs, int64_t gx,
+                                                            int64_t ntiles, int64_t per_xcd) {
+  constexpr int ES = SRC_BF16 ? 2 : 4;
+  constexpr int RW = 128 * ES / 4;                 // dwords per tile row: 64 / 128
+  constexpr int CW = 8 * ES / 4;                   // dwords per chunk: 4 / 8
+  constexpr int SWZ = 2 * ES;                      // dwords of a half-wave's 8 columns
+  extern __shared__ __align__(16) uint32_t dtile[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  // grouped tile order (grouped_tile), XCD chunks: the tiles that share a row's line of
+  // rowwise scale bytes also run on one XCD
+  const int64_t t = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (t >= ntiles) return;                           // the whole workgroup, before any barrier
+  int64_t y, x;
+  grouped_tile<kDualGroupH, kDualGroupW>(t, gx, ntiles / gx, y, x);
+  const int64_t c0 = 128 * x, r0 = 128 * y;
+  const int64_t nb_r = (cols + 31) / 32, nb_c = (rows + 31) / 32;
+  const int64_t kp_r = 32 * nb_r;
+  const int64_t nvalid = rows - r0 < 128 ? rows - r0 : 128;
+  const char* base = reinterpret_cast<const char*>(src) + (r0 * ld_src + c0) * ES;
+  const uint32_t range = (uint32_t)(((nvalid - 1) * ld_src + (cols - c0)) * ES);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)range, 0x00020000);
+  const int row_bytes = (int)(ld_src * ES);
+  const int chunk = tid & 15;
+  const int64_t cc = c0 + 8 * chunk;               // first column of the lane's chunks
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = (tid >> 4) + 16 * q;
+    Chunk<SRC_BF16> ch;
+#pragma unroll
+    for (int h = 0; h < ES / 2; ++h) {             // 16-byte pieces of the chunk
+      const auto d = __builtin_amdgcn_raw_buffer_load_b128(rs, row * row_bytes + (8 * chunk) * ES + 16 * h, 0, 0);
+      const bool in = cc + (16 / ES) * h < cols;   // pieces past cols are padding
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ch.w[4 * h + i] = in ? (uint32_t)d[i] : 0u;
+    }
+    const int sw = SWZ * ((row >> 5) & 3);
+#pragma unroll
+    for (int h = 0; h < ES / 2; ++h)
+      *reinterpret_cast<uint4*>(&dtile[row * RW + ((CW * chunk + 4 * h) ^ sw)]) =
+          make_uint4(ch.w[4 * h], ch.w[4 * h + 1], ch.w[4 * h + 2], ch.w[4 * h + 3]);
+    // rowwise block of this quad (every lane of the wave takes part in the DPP)
+    const uint32_t amax = quad_max(chunk_abs_max<SRC_BF16>(ch));
+    const uint32_t sb = scale_byte_from_amax<F>(amax);
+    uint32_t d0, d1;
+    encode_chunk<SRC_BF16, F>(ch, sb, d0, d1);
+    const int64_t r = r0 + row;
+    if (r < rows && cc < kp_r) {
+      *reinterpret_cast<uint2*>(rcodes + r * ld_rc + cc) = make_uint2(d0, d1);
+      if ((chunk & 3) == 0) rscales[r * ld_rs + (cc >> 5)] = (uint8_t)sb;
+    }
+  }
+  __syncthreads();
+  const int kb = lane & 3;
+  const int64_t b = 4 * y + kb;
+  if (b >= nb_c) return;                           // no barrier follows
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int cl = 64 * u + 16 * wv + (lane >> 2);
+    const int64_t col = c0 + cl;
+    if (col >= cols) break;
+    uint32_t w[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int row = 32 * kb + i;
+      const int sw = SWZ * kb;
+      if (SRC_BF16) w[i] = (uint32_t)reinterpret_cast<const uint16_t*>(dtile)[2 * (row * RW + ((cl >> 1) ^ sw)) + (cl & 1)];
+      else w[i] = dtile[row * RW + (cl ^ sw)];
+    }
+    uint32_t c[8], sb;
+    if (SRC_BF16) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) m = pk_abs_max_bf16(m, w[i]);
+      sb = scale_byte_from_amax<F>(m << 16);
+      encode_block32_bf16_half<F>(w, false, sb, c);
+    } else {
+      uint32_t amax = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t a = w[i] & 0x7FFFFFFFu;
+        amax = amax > a ? amax : a;
+      }
+      sb = scale_byte_from_amax<F>(amax);
+      encode_block32<F>(w, sb, c);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(ccodes + col * ld_cc + 32 * b);
+    dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+    dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+    cscales[col * ld_cs + b] = (uint8_t)sb;
+  }
+}
+
 // Rowwise quantize with stochastically rounded codes: one lane per block as in
 // k_quant_rows; the block's scale byte is the RNE quantizer's, its 32 codes are drawn by
 // encode_sr with the block's Philox words (line l, block b -> block index l * nb + b).
@@ -559,45 +869,74 @@ hipError_t launch_quant_rows(const void* src, int src_bf16, int64_t rows, int64_
 
 template <int SRC_BF16, int F, int R>
 static hipError_t quant_cols_t(const void* src, int64_t rows, int64_t cols, int64_t ld_src, uint8_t* codes,
-                               int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec, hipStream_t stream) {
+                               int64_t ld_codes, uint8_t* scales, int64_t ld_scales, hipStream_t stream) {
+  constexpr int64_t ES = SRC_BF16 ? 2 : 4;
   const int64_t nb = (rows + 31) / 32;
-  const int64_t gx = (cols + kColTileCols - 1) / kColTileCols;
-  int64_t gy = (rows + kColTileRows - 1) / kColTileRows;
-  if (gy > 65535) gy = 65535;
-  if (gx > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (vec)
-    hipLaunchKernelGGL((k_quant_cols<SRC_BF16, F, true, R>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream,
-                       src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales);
+  int64_t grid = 0;
+  const ColTiles tiles = col_tiles(rows, cols, &grid);
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const bool buf = kColGroupRows * ld_src * ES < ((int64_t)1 << 31);
+  const int vsc = (uintptr_t)scales % 16 == 0 && ld_scales % 16 == 0;
+  if ((uintptr_t)src % 16 == 0 && (ld_src * ES) % 16 == 0 && (cols * ES) % 16 == 0 &&
+      128 * ld_src * ES < ((int64_t)1 << 31)) {
+    const int64_t gx = (cols + CtGeom<SRC_BF16>::TC - 1) / CtGeom<SRC_BF16>::TC;
+    const int64_t ntiles = gx * ((rows + 127) / 128);
+    const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
+    if (kXcds * per_xcd > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_quant_cols_lds<SRC_BF16, F, R>), dim3((unsigned)(kXcds * per_xcd)), dim3(kThreads), 0,
+                       stream, src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales, gx, ntiles, per_xcd);
+    return hipGetLastError();
+  }
+  if (buf)
+    hipLaunchKernelGGL((k_quant_cols<SRC_BF16, F, true, R>), dim3((unsigned)grid), dim3(kThreads), 0, stream, src,
+                       rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales, tiles, vsc);
   else
-    hipLaunchKernelGGL((k_quant_cols<SRC_BF16, F, false, R>), dim3((unsigned)gx, (unsigned)gy), dim3(kThreads), 0, stream,
-                       src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales);
+    hipLaunchKernelGGL((k_quant_cols<SRC_BF16, F, false, R>), dim3((unsigned)grid), dim3(kThreads), 0, stream, src,
+                       rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales, tiles, vsc);
   return hipGetLastError();
 }
 
 template <int R>
 static hipError_t quant_cols_r(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, int fmt,
-                               uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec,
+                               uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                                hipStream_t stream) {
   if (src_bf16) {
-    if (fmt == kE4M3) return quant_cols_t<1, kE4M3, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
-    return quant_cols_t<1, kE5M2, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+    if (fmt == kE4M3) return quant_cols_t<1, kE4M3, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, stream);
+    return quant_cols_t<1, kE5M2, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, stream);
   }
-  if (fmt == kE4M3) return quant_cols_t<0, kE4M3, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
-  return quant_cols_t<0, kE5M2, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, vec, stream);
+  if (fmt == kE4M3) return quant_cols_t<0, kE4M3, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, stream);
+  return quant_cols_t<0, kE5M2, R>(src, rows, cols, ld_src, codes, ld_codes, scales, ld_scales, stream);
 }
 
 hipError_t launch_quant_cols(const void* src, int src_bf16, int64_t rows, int64_t cols, int64_t ld_src, int fmt,
-                             int rule, uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, bool vec,
+                             int rule, uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                              hipStream_t stream) {
   if (rule == kRuleOcp)
-    return quant_cols_r<kRuleOcp>(src, src_bf16, rows, cols, ld_src, fmt, codes, ld_codes, scales, ld_scales, vec, stream);
-  return quant_cols_r<kRuleCeil>(src, src_bf16, rows, cols, ld_src, fmt, codes, ld_codes, scales, ld_scales, vec, stream);
+    return quant_cols_r<kRuleOcp>(src, src_bf16, rows, cols, ld_src, fmt, codes, ld_codes, scales, ld_scales, stream);
+  return quant_cols_r<kRuleCeil>(src, src_bf16, rows, cols, ld_src, fmt, codes, ld_codes, scales, ld_scales, stream);
 }
 
 template <int SRC_BF16, int F>
 static hipError_t quant_dual_t(const void* src, int64_t rows, int64_t cols, int64_t ld_src, uint8_t* rcodes,
                                int64_t ld_rc, uint8_t* rscales, int64_t ld_rs, uint8_t* ccodes, int64_t ld_cc,
                                uint8_t* cscales, int64_t ld_cs, bool vec, hipStream_t stream) {
+  constexpr int64_t ES = SRC_BF16 ? 2 : 4;
+  if ((uintptr_t)src % 16 == 0 && (ld_src * ES) % 16 == 0 && (cols * ES) % 16 == 0 &&
+      128 * ld_src * ES < ((int64_t)1 << 31)) {
+    const int64_t gx2 = (cols + 127) / 128;
+    const int64_t ntiles = gx2 * ((rows + 127) / 128);
+    const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
+    if (kXcds * per_xcd > 0x7FFFFFFF) return hipErrorInvalidValue;
+    constexpr int lds = 128 * 128 * (int)ES;
+    auto kern = k_quant_dual_lds<SRC_BF16, F>;
+    if (lds > 65536 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
+            hipSuccess)
+      return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(kXcds * per_xcd)), dim3(kThreads), lds, stream, src, rows, cols, ld_src,
+                       rcodes, ld_rc, rscales, ld_rs, ccodes, ld_cc, cscales, ld_cs, gx2, ntiles, per_xcd);
+    return hipGetLastError();
+  }
   const int64_t gx = (cols + kColTileCols - 1) / kColTileCols;
   int64_t gy = (rows + kColTileRows - 1) / kColTileRows;
   if (gy > 65535) gy = 65535;
