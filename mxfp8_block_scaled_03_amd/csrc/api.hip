@@ -221,7 +221,8 @@ int mxq_gemm_ex(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t
   ep.ld_qs = q_codes ? ld_q_scales : 0;
   ep.q_fmt = q_codes ? to_fmt(q_elem) : 0;
   return hip_status(mxq::launch_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, to_fmt(x_elem), w_codes, ld_w, w_scales,
-                                     ld_ws, to_fmt(w_elem), ep, accum == MXQ_ACC_FP32, (hipStream_t)stream));
+                                     ld_ws, to_fmt(w_elem), ep, accum == MXQ_ACC_FP32, nullptr, 0, true,
+                                     (hipStream_t)stream));
 }
 
 int mxq_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales,

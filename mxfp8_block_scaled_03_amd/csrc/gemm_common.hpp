@@ -32,16 +32,25 @@ extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 // Output tile of workgroup `wg`: consecutive workgroup ids go round-robin over the XCDs,
 // so tile t is given to the workgroups of one XCD first (neighbouring tiles share that
 // XCD's L2), then tiles are walked in groups of kGroupM tile rows, column by column.
-__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int ntiles = tiles_m * tiles_n;
+// Work item `wg` of `count` launched ones -> its index in XCD-major order (the items of
+// one XCD consecutive).
+__device__ __forceinline__ int xcd_order(int wg, int count) {
   const int xcd = wg % kXcds, local = wg / kXcds;
-  const int q = ntiles / kXcds, r = ntiles % kXcds;
-  const int t = xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int q = count / kXcds, r = count % kXcds;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+// Tile number t -> tile (tm, tn): groups of kGroupM tile rows, column by column.
+__device__ __forceinline__ void tile_at(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = kGroupM * tiles_n;
   const int first_m = (t / per_group) * kGroupM;
   const int gsize = min(tiles_m - first_m, kGroupM);
   tm = first_m + (t % per_group) % gsize;
   tn = (t % per_group) / gsize;
+}
+
+__device__ __forceinline__ void tile_of(int wg, int tiles_m, int tiles_n, int& tm, int& tn) {
+  tile_at(xcd_order(wg, tiles_m * tiles_n), tiles_m, tiles_n, tm, tn);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -54,6 +54,20 @@ constexpr int kScaleSlotBytes = 512 * 4;             // X rows 0..255, W rows 25
 constexpr int kScaleSlots = 4;
 constexpr int kLdsBytes = kOffScale + kScaleSlots * kScaleSlotBytes;   // 136 KiB
 constexpr int kEpiWaveBytes = 32768;                 // per-wave epilogue staging (in the code stages)
+constexpr int kPartFloats = 4 * 64 * 256;            // one tile's FP32 accumulators (256 KiB)
+
+// K split of the last round's tiles.  Items 0 .. full-1 are whole tiles (tile numbers
+// 0 .. full-1); items full .. full+halves-1 are the two K halves of tiles full ..: half 0
+// runs stages [0, s_half), half 1 stages [s_half, S).  Each half writes its FP32 sums,
+// row-major 256 x 256, to part[(2 (t - full) + half) * kPartFloats ..] through the
+// epilogue's own store path; a second launch adds the two halves of each split tile and
+// runs the epilogue on the total (k_gemm_ex_fix_ew, or this kernel with fix = 1 when MX
+// codes are written).  No split: full = tiles, halves = 0.
+struct ExSplit {
+  int full, halves, s_half;
+  int fix;          // 1: the fix-up launch (one 64-thread workgroup per wave of a split tile)
+  float* part;
+};
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -91,17 +105,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
                                                         const uint8_t* __restrict__ xs, int64_t ld_xs,
                                                         const uint8_t* __restrict__ wc, int64_t ld_w,
                                                         const uint8_t* __restrict__ ws, int64_t ld_ws,
-                                                        const GemmEpilogue ep) {
+                                                        const GemmEpilogue ep, const ExSplit sp) {
+  // work item -> tile and K-stage range [s0, s0 + S); the fix-up launch takes tile
+  // full + blockIdx.x and no stages
+  const int S_all = (K + 63) / 64;          // stages of the whole K
+  int t, half = -1;
+  if (sp.fix) {
+    t = sp.full + (int)(blockIdx.x >> 2);
+  } else if ((int)blockIdx.x < sp.full) {
+    t = xcd_order(blockIdx.x, sp.full);
+  } else {
+    const int k = xcd_order(blockIdx.x - sp.full, sp.halves);
+    t = sp.full + (k >> 1);
+    half = k & 1;
+  }
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_at(t, tiles_m, tiles_n, tm, tn);
+  const int s0 = half == 1 ? sp.s_half : 0;
+  const int S = sp.fix ? 0 : (half == 0 ? sp.s_half : S_all - s0);   // stages of this item
+  const int P0 = s0 >> 1;                   // its first scale word (s_half is even)
+  const bool last_range = half != 0;        // holds the last stage
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the fix-up launch runs one wave per workgroup (4 per tile): its wave index comes from
+  // the workgroup index, and its epilogue staging uses LDS slot 0
+  const int wid = sp.fix ? (int)(blockIdx.x & 3) : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wslot = sp.fix ? 0 : wid;
   const int wm = wid >> 1, wn = wid & 1;
   const int li = lane & 31, lg = lane >> 5;
   const int nb = (K + 31) / 32;             // blocks per line
   const int Kp = 32 * nb;
-  const int S = (K + 63) / 64;              // stages
   const int nbf = nb / 4;                   // whole 4-block scale words per row
   const int rows_x = min(BM, M - m0), rows_w = min(BN, N - n0);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
@@ -119,8 +152,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      voff_x[n] = (uint32_t)((drow + 16 * n) * ld_x + 16 * dchunk);
-      voff_w[n] = (uint32_t)((drow + 16 * n) * ld_w + 16 * dchunk);
+      voff_x[n] = (uint32_t)((drow + 16 * n) * ld_x + 16 * dchunk + 64 * s0);
+      voff_w[n] = (uint32_t)((drow + 16 * n) * ld_w + 16 * dchunk + 64 * s0);
     }
   }
   const uint32_t lds_cx = lds0 + (uint32_t)(64 * wid) * 64;   // + stage slot + 1024 n
@@ -139,7 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   const int s_words = s_last_tile ? nbf : (nb + 3) / 4;        // words of the descriptor's last row
   uint32_t voff_s[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) voff_s[h] = (uint32_t)((128 * (wid & 1) + 64 * h + lane) * ld_s);
+  for (int h = 0; h < 2; ++h) voff_s[h] = (uint32_t)((128 * (wid & 1) + 64 * h + lane) * ld_s + 4 * P0);
   const uint32_t lds_s = lds0 + kOffScale + (uint32_t)(128 * wid) * 4;   // + slot + 256 h
 
   // One descriptor per operand for the whole K loop, the K offset in the lane offset: a
@@ -225,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   // the last row's partial word replaces what the DMA left there (zeros); branch free, so
   // no conversion is moved across it
   auto fix_scale = [&](int P) __attribute__((always_inline)) {
-    const bool last_word = P == nbf;
+    const bool last_word = P + P0 == nbf;
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       sdw[f] = (last_word && tail_fx == f) ? tail_x : sdw[f];
@@ -265,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   auto mask_last_stage = [&]() __attribute__((always_inline)) {
     const int r = threadIdx.x;
     if (nb & 1) {
-      const int P = nb >> 2;
+      const int P = (nb >> 2) - P0;
       const uint32_t a = (uint32_t)kOffScale + (uint32_t)(P & 3) * kScaleSlotBytes + (uint32_t)(nb & 3);
       smem[a + 4u * (uint32_t)r] = 127;
       smem[a + 4u * (uint32_t)(256 + r)] = 127;
@@ -275,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     for (int op = 0; op < 2; ++op) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int lim = K - (64 * (S - 1) + 16 * c);
+        const int lim = K - (64 * (s0 + S - 1) + 16 * c);
         if (lim < 16) {
           v4i* q = reinterpret_cast<v4i*>(smem + so + (uint32_t)(op * kOpBytes + r * 64) +
                                           (uint32_t)((c ^ ((r >> 2) & 3)) << 4));
@@ -311,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     // stage 0 and scale word 0 landed: 25 loads were issued after stage 0's codes
     wait_vm<25>();
     lds_barrier();
-    if (K < 64 * S) {
+    if (last_range && K < 64 * S_all) {
       if (S == 1) {
         mask_last_stage();
         lds_barrier();
@@ -353,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
       // has finished reading stage s, whose slot the DMA of stage s+4 now reuses
       wait_vm<19>();
       lds_barrier();
-      if (K < 64 * S) {
+      if (last_range && K < 64 * S_all) {
         if (s == S - 2) {
           mask_last_stage();
           lds_barrier();
@@ -402,13 +435,48 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     wait_vm<0>();
     lds_barrier();
   }
+  if (sp.fix) {
+    // the two K halves of the tile, row-major 256 x 256 FP32 in the workspace: their sums
+    // added (the order of two addends does not change an FP32 sum)
+    const float* p0 = sp.part + (int64_t)(2 * (t - sp.full)) * kPartFloats;
+    const float* p1 = p0 + kPartFloats;
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < 4; ++fj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typedef float v4f __attribute__((ext_vector_type(4)));
+          const int off = (128 * wm + 32 * fi + li) * 256 + 128 * wn + 32 * fj + 8 * q + 4 * lg;
+          const v4f a = *reinterpret_cast<const v4f*>(p0 + off), b = *reinterpret_cast<const v4f*>(p1 + off);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[fi][fj][4 * q + e] = a[e] + b[e];
+        }
+  }
+  // a K half writes its FP32 sums through the epilogue's own store path: alpha 1 (exact),
+  // no bias, activation or codes, fp32 rows of 256 into its slot of the workspace
+  GemmEpilogue epx = ep;
+  int Mx = M, Nx = N, m0x = m0, n0x = n0;
+  if (half >= 0) {
+    epx.alpha = 1.0f;
+    epx.bias = nullptr;
+    epx.act = 0;
+    epx.y = sp.part + (int64_t)(2 * (t - sp.full) + half) * kPartFloats;
+    epx.y_bf16 = 0;
+    epx.ld_y = 256;
+    epx.y_vec16 = 1;
+    epx.qc = nullptr;
+    epx.qs = nullptr;
+    Mx = Nx = 256;
+    m0x = n0x = 0;
+  }
 
   // ---- epilogue: v = act(alpha * acc + bias[col]) in place.  Lane (g, i) holds
   //      Y[row 32 fi + i][col 32 fj + 8 q + 4 g + e] in acc[fi][fj][4 q + e], rows and
   //      columns relative to the wave's 128x128 block.
-  const int wrow0 = m0 + 128 * wm, wcol0 = n0 + 128 * wn;
+  const int wrow0 = m0x + 128 * wm, wcol0 = n0x + 128 * wn;
   {
-    const bool has_bias = ep.bias != nullptr;
+    const bool has_bias = epx.bias != nullptr;
 #pragma unroll
     for (int fj = 0; fj < 4; ++fj)
 #pragma unroll
@@ -416,14 +484,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int col = wcol0 + 32 * fj + 8 * q + 4 * lg + e;
-          const float bv = (has_bias && col < N) ? ep.bias[col] : 0.0f;
+          const float bv = (has_bias && col < Nx) ? epx.bias[col] : 0.0f;
 #pragma unroll
           for (int fi = 0; fi < 4; ++fi) {
             const float a = acc[fi][fj][4 * q + e];
-            acc[fi][fj][4 * q + e] = has_bias ? __builtin_fmaf(ep.alpha, a, bv) : ep.alpha * a;
+            acc[fi][fj][4 * q + e] = has_bias ? __builtin_fmaf(epx.alpha, a, bv) : epx.alpha * a;
           }
         }
-    if (ep.act) {
+    if (epx.act) {
 #pragma unroll
       for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
@@ -432,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
           for (int r = 0; r < 16; ++r) acc[fi][fj][r] = silu(acc[fi][fj][r]);
     }
   }
-  const uint32_t wbase = (uint32_t)wid * kEpiWaveBytes;
+  const uint32_t wbase = (uint32_t)wslot * kEpiWaveBytes;
   auto wave_lds_sync = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
     __builtin_amdgcn_wave_barrier();
@@ -452,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
         const int c0 = 32 * fjl + 8 * q + 4 * lg;           // first of this lane's 4 staged columns
         bool in[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) in[e] = !zero_past_n || wcol0 + 32 * fj + 8 * q + 4 * lg + e < N;
+        for (int e = 0; e < 4; ++e) in[e] = !zero_past_n || wcol0 + 32 * fj + 8 * q + 4 * lg + e < Nx;
 #pragma unroll
         for (int fi = 0; fi < 4; ++fi) {
           const int row = 32 * fi + li;
@@ -477,8 +545,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
         }
       }
   };
-  if (!ep.y) {
-  } else if (ep.y_vec16 && m0 + BM <= M && n0 + BN <= N) {
+  if (!epx.y) {
+  } else if (epx.y_vec16 && m0x + BM <= Mx && n0x + BN <= Nx) {
     // interior tile, aligned y: staged rows stored as whole 16-byte pieces
     auto store_pass = [&](auto e_c, int pass) __attribute__((always_inline)) {
       constexpr int E = decltype(e_c)::value;
@@ -489,13 +557,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
         const int row = 4 * it + (lane >> 4), c = lane & 15;
         const v4i v = *reinterpret_cast<const v4i*>(smem + wbase + (uint32_t)row * 256u +
                                                     ((uint32_t)(c ^ (row & 7)) << 4));
-        uint8_t* dst = reinterpret_cast<uint8_t*>(ep.y) +
-                       ((int64_t)(wrow0 + row) * ep.ld_y + wcol0 + (E == 2 ? 0 : 64 * pass)) * E + 16 * c;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(epx.y) +
+                       ((int64_t)(wrow0 + row) * epx.ld_y + wcol0 + (E == 2 ? 0 : 64 * pass)) * E + 16 * c;
         *reinterpret_cast<v4i*>(dst) = v;
       }
       wave_lds_sync();
     };
-    if (ep.y_bf16) {
+    if (epx.y_bf16) {
       store_pass(std::integral_constant<int, 2>(), 0);
     } else {
       store_pass(std::integral_constant<int, 4>(), 0);
@@ -512,29 +580,80 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
 #pragma unroll
           for (int fi = 0; fi < 4; ++fi) {
             const int row = wrow0 + 32 * fi + li;
-            if (row < M && col < N) {
+            if (row < Mx && col < Nx) {
               const float v = acc[fi][fj][4 * q + e];
-              if (ep.y_bf16)
-                reinterpret_cast<uint16_t*>(ep.y)[(int64_t)row * ep.ld_y + col] = (uint16_t)f32_to_bf16_rne(v);
+              if (epx.y_bf16)
+                reinterpret_cast<uint16_t*>(epx.y)[(int64_t)row * epx.ld_y + col] = (uint16_t)f32_to_bf16_rne(v);
               else
-                reinterpret_cast<float*>(ep.y)[(int64_t)row * ep.ld_y + col] = v;
+                reinterpret_cast<float*>(epx.y)[(int64_t)row * epx.ld_y + col] = v;
             }
           }
         }
   }
-  if (ep.qc) {
+  if (epx.qc) {
     // bf16(v) of the wave's block staged as 128 rows of 128 values, columns >= N as +0,
     // then quantized along the rows in 32-column blocks
     stage_rows(std::integral_constant<int, 2>(), 0, true);
     wave_lds_sync();
-    quantize_staged<4>(wbase, lane, wrow0, M, wcol0 / 32, (N + 31) / 32, ep);
+    quantize_staged<4>(wbase, lane, wrow0, Mx, wcol0 / 32, (Nx + 31) / 32, epx);
   }
+}
+
+// Fix-up of the split tiles when no MX codes are written: elementwise over the tiles'
+// 256 x 256 outputs, 4 consecutive columns per thread, 64 workgroups per tile.
+// v = act(alpha * (h0 + h1) + bias[col]), rounded and stored as the epilogue of
+// k_gemm_ex does it (the same FP32 operations in the same order, so the same bits).
+__global__ __launch_bounds__(256) void k_gemm_ex_fix_ew(int M, int N, int tiles_m, int tiles_n, const GemmEpilogue ep,
+                                                       const ExSplit sp) {
+  const int j = (int)(blockIdx.x >> 6);                 // split tile
+  const int e0 = (int)((blockIdx.x & 63) * 1024 + 4 * threadIdx.x);   // element of the tile
+  const int r = e0 >> 8, c = e0 & 255;
+  int tm, tn;
+  tile_at(sp.full + j, tiles_m, tiles_n, tm, tn);
+  const int row = tm * BM + r, col0 = tn * BN + c;
+  if (row >= M || col0 >= N) return;
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  const float* p0 = sp.part + (int64_t)(2 * j) * kPartFloats + e0;
+  const v4f a = *reinterpret_cast<const v4f*>(p0), b = *reinterpret_cast<const v4f*>(p0 + kPartFloats);
+  const bool has_bias = ep.bias != nullptr;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int col = col0 + e;
+    if (col >= N) break;
+    const float acc = a[e] + b[e];
+    float v = has_bias ? __builtin_fmaf(ep.alpha, acc, ep.bias[col]) : ep.alpha * acc;
+    if (ep.act) v = silu(v);
+    if (ep.y_bf16)
+      reinterpret_cast<uint16_t*>(ep.y)[(int64_t)row * ep.ld_y + col] = (uint16_t)f32_to_bf16_rne(v);
+    else
+      reinterpret_cast<float*>(ep.y)[(int64_t)row * ep.ld_y + col] = v;
+  }
+}
+
+// K split of the last round: with P workgroups resident at once (one per CU) and T tiles,
+// the last round holds R = T mod P tiles.  When there is more than one round and
+// R <= P / 2, those tiles run as 2R K halves (of at least 4 stages each), so the last
+// round takes half a tile's time instead of a whole one.
+ExSplit plan_split(int64_t tiles, int64_t K, int cus) {
+  ExSplit sp;
+  sp.full = (int)tiles;
+  sp.halves = 0;
+  sp.s_half = 0;
+  sp.fix = 0;
+  sp.part = nullptr;
+  const int64_t S = (K + 63) / 64, R = cus > 0 ? tiles % cus : 0;
+  if (tiles > cus && R > 0 && 2 * R <= cus && S >= 8) {
+    sp.full = (int)(tiles - R);
+    sp.halves = (int)(2 * R);
+    sp.s_half = (int)(2 * (S / 4));          // even: a whole number of scale words
+  }
+  return sp;
 }
 
 template <int FA, int FB>
 hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
                     int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
-                    const GemmEpilogue& ep, hipStream_t stream) {
+                    const GemmEpilogue& ep, const ExSplit& sp, hipStream_t stream) {
   static bool attr_set[64] = {false};
   auto kern = k_gemm_ex<FA, FB>;
   int dev = 0;
@@ -545,22 +664,52 @@ hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t 
     attr_set[dev] = true;
   }
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL(kern, dim3(tiles_m * tiles_n), dim3(kThreads), kLdsBytes, stream, (int)M, (int)N, (int)K, tiles_m,
-                     tiles_n, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep);
+  hipLaunchKernelGGL(kern, dim3(sp.full + sp.halves), dim3(kThreads), kLdsBytes, stream, (int)M, (int)N, (int)K,
+                     tiles_m, tiles_n, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp.halves == 0) return e;
+  if (!ep.qc) {
+    // plain outputs: the elementwise fix-up (64 workgroups per split tile)
+    hipLaunchKernelGGL(k_gemm_ex_fix_ew, dim3(32 * sp.halves), dim3(256), 0, stream, (int)M, (int)N, tiles_m, tiles_n,
+                       ep, sp);
+    return hipGetLastError();
+  }
+  // with MX codes: the kernel's own epilogue, one wave per workgroup, four per split tile,
+  // 32 KiB of LDS each, so every CU takes part (one 4-wave workgroup per tile left half
+  // the CUs idle)
+  ExSplit fx = sp;
+  fx.fix = 1;
+  hipLaunchKernelGGL(kern, dim3(2 * sp.halves), dim3(64), kEpiWaveBytes, stream, (int)M, (int)N, (int)K, tiles_m,
+                     tiles_n, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, fx);
   return hipGetLastError();
 }
 
 }  // namespace ex
 }  // namespace
 
+int64_t gemm_exact_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + ex::BM - 1) / ex::BM) * ((N + ex::BN - 1) / ex::BN);
+  const ex::ExSplit sp = ex::plan_split(tiles, K, device_cu_count());
+  return (int64_t)sp.halves * ex::kPartFloats * (int64_t)sizeof(float);
+}
+
 hipError_t launch_gemm_exact(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
                              int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws,
-                             int64_t ld_ws, int w_fmt, const GemmEpilogue& ep, hipStream_t stream) {
+                             int64_t ld_ws, int w_fmt, const GemmEpilogue& ep, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream) {
+  const int64_t tiles = ((M + ex::BM - 1) / ex::BM) * ((N + ex::BN - 1) / ex::BN);
+  ex::ExSplit sp = ex::plan_split(tiles, K, device_cu_count());
+  if (sp.halves > 0) {
+    if (workspace == nullptr || workspace_bytes < (int64_t)sp.halves * ex::kPartFloats * (int64_t)sizeof(float))
+      sp = ex::plan_split(tiles, K, 0);       // no room: the whole tiles only
+    else
+      sp.part = static_cast<float*>(workspace);
+  }
   if (x_fmt == kE4M3 && w_fmt == kE4M3)
-    return ex::launch_f<0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
-  if (x_fmt == kE4M3) return ex::launch_f<0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
-  if (w_fmt == kE4M3) return ex::launch_f<1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
-  return ex::launch_f<1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, stream);
+    return ex::launch_f<0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
+  if (x_fmt == kE4M3) return ex::launch_f<0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
+  if (w_fmt == kE4M3) return ex::launch_f<1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
+  return ex::launch_f<1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
 }
 
 }  // namespace mxq

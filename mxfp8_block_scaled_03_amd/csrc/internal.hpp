@@ -67,9 +67,13 @@ struct GemmEpilogue {
 };
 
 // The GEMM kernels (gemm_exact.hip, gemm_fp8.hip, gemm_fallback.hip); launch_gemm picks one.
+// Exact-product GEMM.  workspace: device memory for the K split of the last round's tiles
+// (gemm_exact_workspace_bytes(M, N, K) bytes; with less, or none, the tiles run whole).
+int64_t gemm_exact_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_exact(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
                              int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws,
-                             int64_t ld_ws, int w_fmt, const GemmEpilogue& ep, hipStream_t stream);
+                             int64_t ld_ws, int w_fmt, const GemmEpilogue& ep, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream);
 hipError_t launch_gemm_fp8(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
                            int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
                            int w_fmt, const GemmEpilogue& ep, hipStream_t stream);
@@ -77,9 +81,12 @@ hipError_t launch_gemm_fallback(int64_t M, int64_t N, int64_t K, const uint8_t* 
                                 int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws,
                                 int64_t ld_ws, int w_fmt, const GemmEpilogue& ep, int exact, hipStream_t stream);
 
+// workspace / workspace_bytes: device memory the exact kernel may use for its K split;
+// may_alloc: when it is too small, take one from the stream-ordered pool for the call.
 hipError_t launch_gemm(int64_t M, int64_t N, int64_t K,
                        const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_fmt,
                        const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws, int w_fmt,
-                       const GemmEpilogue& ep, int exact, hipStream_t stream);
+                       const GemmEpilogue& ep, int exact, void* workspace, int64_t workspace_bytes, bool may_alloc,
+                       hipStream_t stream);
 
 }  // namespace mxq
