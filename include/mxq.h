@@ -21,8 +21,12 @@
  *
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library never
- *     allocates, frees or synchronizes; work is enqueued on `stream` (a hipStream_t
- *     passed as void*; NULL means the default stream) and runs asynchronously.
+ *     synchronizes; work is enqueued on `stream` (a hipStream_t passed as void*; NULL
+ *     means the default stream) and runs asynchronously.  Nothing is allocated, except
+ *     the workspace of mxq_gemm / mxq_gemm_ex in the MXQ_ACC_FP32 mode when it splits the
+ *     last round of tiles along K (see mxq_gemm_ex), which is taken from and given back
+ *     to the device's stream-ordered memory pool on `stream` (hipMallocAsync /
+ *     hipFreeAsync); mxq_gemm_ex_noalloc allocates nothing.
  *   - Sizes and leading dimensions are in ELEMENTS of the pointed-to type (bytes for
  *     code and scale arrays).  K is the contraction (block) axis, Kp = 32*ceil(K/32)
  *     and nb = Kp/32 is the number of blocks per line.
@@ -53,7 +57,8 @@ typedef enum {
   MXQ_ERR_ALIGN = -4,  /* a pointer or leading dimension breaks the stated alignment */
   MXQ_ERR_DTYPE = -5,  /* a dtype tag that the entry point does not accept         */
   MXQ_ERR_ARG = -6,    /* any other invalid argument (axis, non-finite alpha)      */
-  MXQ_ERR_HIP = -7     /* the HIP runtime reported an error when enqueuing          */
+  MXQ_ERR_HIP = -7,    /* the HIP runtime reported an error when enqueuing          */
+  MXQ_ERR_SCRATCH = -8 /* mxq_gemm_ex_noalloc: more workspace than its static scratch */
 } mxq_status;
 
 typedef enum {
@@ -295,6 +300,15 @@ typedef enum { MXQ_ACT_NONE = 0, MXQ_ACT_SILU = 1 } mxq_act;
  *          q_codes 16-byte aligned, ld_q_scales >= Np/32; codes of columns N..Np-1 are 0.
  * At least one of y and q_codes must be given (MXQ_ERR_NULL otherwise).  Writing only
  * the codes saves the wide output's write and the quantize pass's read of it.
+ *
+ * Tile rounds (MXQ_ACC_FP32 with 4-byte aligned scale rows).  The output is computed in
+ * 256 x 256 tiles, one per CU at a time.  When there are more tiles than CUs and the last
+ * round holds at most half as many tiles as there are CUs, each of those tiles is
+ * computed as two halves of the K range, whose FP32 sums are added (FP32) before the
+ * epilogue: the result stays within the same bound and is deterministic for a given
+ * device, but its rounding differs from the unsplit order.  The halves' sums go to a
+ * workspace of 256 KiB per half tile, taken from the stream-ordered pool for the call;
+ * if that allocation fails the tiles run whole.
  */
 int mxq_gemm_ex(int64_t M, int64_t N, int64_t K,
                 const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_elem,
@@ -303,6 +317,26 @@ int mxq_gemm_ex(int64_t M, int64_t N, int64_t K,
                 void* y, int y_type, int64_t ld_y,
                 int q_elem, uint8_t* q_codes, int64_t ld_q_codes, uint8_t* q_scales, int64_t ld_q_scales,
                 int accum, void* stream);
+
+/*
+ * mxq_gemm_ex_noalloc -- mxq_gemm_ex that allocates nothing, for callers that cannot call
+ * hipMalloc or hipMallocAsync: work recorded under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.
+ *
+ * Arguments, results and errors as for mxq_gemm_ex, bit for bit.  The K split's workspace
+ * is a file-scope device array of 64 MiB (enough for a device of up to 256 CUs) that
+ * every device the library runs on holds from load until the process ends; a problem
+ * that would need more returns MXQ_ERR_SCRATCH.  All calls on one device share that
+ * array: calls that may overlap on one device (different streams, no ordering between
+ * them) race and must not be made.  No part of the array has to start at any value.
+ */
+int mxq_gemm_ex_noalloc(int64_t M, int64_t N, int64_t K,
+                        const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_elem,
+                        const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales, int64_t ld_ws, int w_elem,
+                        float alpha, const float* bias, int act,
+                        void* y, int y_type, int64_t ld_y,
+                        int q_elem, uint8_t* q_codes, int64_t ld_q_codes, uint8_t* q_scales, int64_t ld_q_scales,
+                        int accum, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* mxq_status_string(int status);

@@ -62,6 +62,8 @@ def lib():
         L.mxq_gemm_ex.restype = ci
         L.mxq_gemm_ex.argtypes = [i64, i64, i64, vp, i64, vp, i64, ci, vp, i64, vp, i64, ci,
                                   ctypes.c_float, vp, ci, vp, ci, i64, ci, vp, i64, vp, i64, ci, vp]
+        L.mxq_gemm_ex_noalloc.restype = ci
+        L.mxq_gemm_ex_noalloc.argtypes = L.mxq_gemm_ex.argtypes
         L.mxq_status_string.restype = ctypes.c_char_p
         L.mxq_status_string.argtypes = [ci]
         L.mxq_version.restype = ci
@@ -118,6 +120,14 @@ def mxq_gemm_ex(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, 
     return lib().mxq_gemm_ex(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws,
                              w_elem, alpha, bias, act, y, y_type, ld_y, q_elem, q_codes, ld_q_codes, q_scales,
                              ld_q_scales, accum, stream)
+
+
+def mxq_gemm_ex_noalloc(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws, w_elem,
+                        alpha, bias, act, y, y_type, ld_y, q_elem, q_codes, ld_q_codes, q_scales, ld_q_scales,
+                        accum=MXQ_ACC_FP32, stream=None) -> int:
+    return lib().mxq_gemm_ex_noalloc(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws,
+                                     w_elem, alpha, bias, act, y, y_type, ld_y, q_elem, q_codes, ld_q_codes, q_scales,
+                                     ld_q_scales, accum, stream)
 
 
 def mxq_status_string(status: int) -> str:

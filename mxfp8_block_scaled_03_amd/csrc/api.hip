@@ -1,5 +1,7 @@
 // api.hip -- the C ABI declared in include/mxq.h: host-side argument validation and
-// dispatch to the gfx950 kernels.  Nothing here allocates, frees or synchronizes.
+// dispatch to the gfx950 kernels.  Nothing here synchronizes; the only allocation is the
+// exact GEMM's split workspace (gemm.hip), which mxq_gemm_ex_noalloc takes from the
+// static `scratch` array below instead.
 #include "mxq.h"
 
 #include <math.h>
@@ -39,11 +41,12 @@ const char* mxq_status_string(int status) {
     case MXQ_ERR_DTYPE: return "MXQ_ERR_DTYPE: dtype tag not accepted here";
     case MXQ_ERR_ARG: return "MXQ_ERR_ARG: invalid argument";
     case MXQ_ERR_HIP: return "MXQ_ERR_HIP: HIP runtime error while enqueuing";
+    case MXQ_ERR_SCRATCH: return "MXQ_ERR_SCRATCH: the problem needs more workspace than the static scratch holds";
     default: return "unknown mxq status";
   }
 }
 
-int mxq_version(void) { return 101; }
+int mxq_version(void) { return 102; }
 
 int mxq_quantize(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int axis, int elem,
                  uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, void* stream) {
@@ -171,11 +174,42 @@ int mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales
                                         dst_type == MXQ_BF16, ld_dst, vec, (hipStream_t)stream));
 }
 
-int mxq_gemm_ex(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales,
-                int64_t ld_xs, int x_elem, const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales,
-                int64_t ld_ws, int w_elem, float alpha, const float* bias, int act, void* y, int y_type,
-                int64_t ld_y, int q_elem, uint8_t* q_codes, int64_t ld_q_codes, uint8_t* q_scales,
-                int64_t ld_q_scales, int accum, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Static workspace for mxq_gemm_ex_noalloc: enough for the K split of the exact GEMM on a
+// device of up to 256 CUs (at most 256 half tiles of 256 x 256 FP32 sums).  A file-scope
+// device array: each device the library runs on holds its own copy from load to exit.
+constexpr int64_t kScratchBytes = (int64_t)256 * 256 * 256 * 4;   // 64 MiB
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The device address of this device's copy of `scratch`, looked up once per device (the
+// array's name in host code is not a device address).  nullptr if the lookup fails.
+void* scratch_on_current_device() {
+  static void* ptr[64] = {nullptr};
+  static bool looked[64] = {false};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (!looked[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    ptr[dev] = p;
+    looked[dev] = true;
+  }
+  return ptr[dev];
+}
+
+// mxq_gemm_ex's validation and dispatch; noalloc: the workspace is `scratch`, and nothing
+// is allocated.
+int gemm_ex_impl(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales,
+                 int64_t ld_xs, int x_elem, const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales,
+                 int64_t ld_ws, int w_elem, float alpha, const float* bias, int act, void* y, int y_type,
+                 int64_t ld_y, int q_elem, uint8_t* q_codes, int64_t ld_q_codes, uint8_t* q_scales,
+                 int64_t ld_q_scales, int accum, void* stream, bool noalloc) {
   if (!is_elem(x_elem) || !is_elem(w_elem)) return MXQ_ERR_DTYPE;
   if (y && !is_wide(y_type)) return MXQ_ERR_DTYPE;
   if (q_codes && !is_elem(q_elem)) return MXQ_ERR_DTYPE;
@@ -220,9 +254,41 @@ int mxq_gemm_ex(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t
   ep.qs = q_codes ? q_scales : nullptr;
   ep.ld_qs = q_codes ? ld_q_scales : 0;
   ep.q_fmt = q_codes ? to_fmt(q_elem) : 0;
+  void* ws = nullptr;
+  int64_t ws_bytes = 0;
+  if (noalloc && accum == MXQ_ACC_FP32) {
+    if (mxq::gemm_exact_workspace_bytes(M, N, K) > kScratchBytes) return MXQ_ERR_SCRATCH;
+    ws = scratch_on_current_device();
+    if (!ws) return MXQ_ERR_HIP;
+    ws_bytes = kScratchBytes;
+  }
   return hip_status(mxq::launch_gemm(M, N, K, x_codes, ld_x, x_scales, ld_xs, to_fmt(x_elem), w_codes, ld_w, w_scales,
-                                     ld_ws, to_fmt(w_elem), ep, accum == MXQ_ACC_FP32, nullptr, 0, true,
+                                     ld_ws, to_fmt(w_elem), ep, accum == MXQ_ACC_FP32, ws, ws_bytes, !noalloc,
                                      (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxq_gemm_ex(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales,
+                int64_t ld_xs, int x_elem, const uint8_t* w_codes, int64_t ld_w, const uint8_t* w_scales,
+                int64_t ld_ws, int w_elem, float alpha, const float* bias, int act, void* y, int y_type,
+                int64_t ld_y, int q_elem, uint8_t* q_codes, int64_t ld_q_codes, uint8_t* q_scales,
+                int64_t ld_q_scales, int accum, void* stream) {
+  return gemm_ex_impl(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws, w_elem, alpha,
+                      bias, act, y, y_type, ld_y, q_elem, q_codes, ld_q_codes, q_scales, ld_q_scales, accum, stream,
+                      false);
+}
+
+int mxq_gemm_ex_noalloc(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x,
+                        const uint8_t* x_scales, int64_t ld_xs, int x_elem, const uint8_t* w_codes, int64_t ld_w,
+                        const uint8_t* w_scales, int64_t ld_ws, int w_elem, float alpha, const float* bias, int act,
+                        void* y, int y_type, int64_t ld_y, int q_elem, uint8_t* q_codes, int64_t ld_q_codes,
+                        uint8_t* q_scales, int64_t ld_q_scales, int accum, void* stream) {
+  return gemm_ex_impl(M, N, K, x_codes, ld_x, x_scales, ld_xs, x_elem, w_codes, ld_w, w_scales, ld_ws, w_elem, alpha,
+                      bias, act, y, y_type, ld_y, q_elem, q_codes, ld_q_codes, q_scales, ld_q_scales, accum, stream,
+                      true);
 }
 
 int mxq_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales,

@@ -18,7 +18,7 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert {"mxq_quantize", "mxq_quantize_rule", "mxq_quantize_dual", "mxq_quantize_sr", "mxq_quantize_scaled", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex",
+    assert {"mxq_quantize", "mxq_quantize_rule", "mxq_quantize_dual", "mxq_quantize_sr", "mxq_quantize_scaled", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex", "mxq_gemm_ex_noalloc",
             "mxq_status_string", "mxq_version"} <= set(declared_symbols())
 
 
@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert mxq.mxq_version() >= 100
-    for st in range(-7, 1):
+    for st in range(-8, 1):
         s = mxq.mxq_status_string(st)
         assert s.startswith("MXQ_")
     assert "unknown" in mxq.mxq_status_string(-99)
@@ -199,9 +199,18 @@ def gx(**kw):
              ld_ws=2, we=mxq.MXQ_E4M3, alpha=1.0, bias=None, act=mxq.MXQ_ACT_SILU, y=None, yt=mxq.MXQ_BF16, ld_y=0,
              qe=mxq.MXQ_E4M3, qc=FAKE, ld_qc=64, qs=FAKE, ld_qs=2, acc=0)     # N = 40 -> Np = 64
     a.update(kw)
-    return mxq.mxq_gemm_ex(a["M"], a["N"], a["K"], a["xc"], a["ld_x"], a["xs"], a["ld_xs"], a["xe"], a["wc"],
-                           a["ld_w"], a["ws"], a["ld_ws"], a["we"], a["alpha"], a["bias"], a["act"], a["y"],
-                           a["yt"], a["ld_y"], a["qe"], a["qc"], a["ld_qc"], a["qs"], a["ld_qs"], a["acc"], None)
+    fn = a.pop("fn", mxq.mxq_gemm_ex)
+    return fn(a["M"], a["N"], a["K"], a["xc"], a["ld_x"], a["xs"], a["ld_xs"], a["xe"], a["wc"],
+              a["ld_w"], a["ws"], a["ld_ws"], a["we"], a["alpha"], a["bias"], a["act"], a["y"],
+              a["yt"], a["ld_y"], a["qe"], a["qc"], a["ld_qc"], a["qs"], a["ld_qs"], a["acc"], None)
+
+
+def test_gemm_ex_noalloc_validates_like_gemm_ex():
+    """The allocation-free variant rejects exactly what mxq_gemm_ex rejects, on the host."""
+    cases = [dict(act=2), dict(qe=mxq.MXQ_BF16), dict(qc=None), dict(ld_qc=48), dict(ld_qc=72), dict(y=FAKE, ld_y=39),
+             dict(alpha=float("inf")), dict(acc=3), dict(K=-1), dict(M=0, xc=None, qc=None, qs=None)]
+    for c in cases:
+        assert gx(fn=mxq.mxq_gemm_ex_noalloc, **c) == gx(**c), c
 
 
 def test_gemm_ex_validation():
