@@ -23,7 +23,8 @@ counter passes profile.
 
 --only quantize_2p28 | quantize_2p28_colwise | quantize_2p28_dual runs that one quantize
 launch on the [16384][16384] bf16 input, W untimed then K timed, and prints its time and
-GB/s (the short run that the quantize kernels' counter passes profile).
+GB/s; --only gemm_exact | gemm_fp8 runs that GEMM mode alone on the projection workload
+(the short runs that the kernels' counter passes profile).
 
 --copy-calibration adds a plain elementwise copy of a known size (256 MiB read, 256 MiB
 written) after the measurement, so that one hardware-counter run sees both the GEMM and a
@@ -62,27 +63,38 @@ def parse():
     return p.parse_args()
 
 
-# --only: one quantize entry point on the [16384][16384] bf16 input, E4M3
-ONLY_KERNELS = {"quantize_2p28": "rowwise", "quantize_2p28_colwise": "colwise", "quantize_2p28_dual": "dual"}
+# --only: one quantize entry point on the [16384][16384] bf16 input, E4M3, or one GEMM
+# mode on the projection workload
+ONLY_KERNELS = {"quantize_2p28": "rowwise", "quantize_2p28_colwise": "colwise", "quantize_2p28_dual": "dual",
+                "gemm_exact": "exact", "gemm_fp8": "fp8"}
 
 
-GEMM_SOURCE = os.path.join(ROOT, "mxfp8_block_scaled_03_amd", "csrc", "gemm.hip")
+_CSRC = os.path.join(ROOT, "mxfp8_block_scaled_03_amd", "csrc")
+# the sources a recorded HBM-traffic measurement was taken on, per kernel
+KERNEL_SOURCES = {
+    "gemm_exact": [os.path.join(_CSRC, "gemm_exact.hip"), os.path.join(_CSRC, "gemm_common.hpp")],
+    "gemm_fp8": [os.path.join(_CSRC, "gemm_fp8.hip"), os.path.join(_CSRC, "gemm_common.hpp")],
+}
 GEMM_KERNEL_NAME = "mxq gemm, exact-product mode (ex::k_gemm_ex<0,0>: codes decoded to bf16 in registers, bf16 matrix cores)"
 FP8_LABEL = "FP8 matrix cores, 8-product groups truncated ~13 bits below their largest (outside 1e-5*T)"
 
 
-def source_digest(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_digest(paths) -> str:
+    """sha256 over the bytes of the given source files, in order."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic(kernel: str):
     """HBM bytes per launch of `kernel` measured with rocprofv3 counters (profiles/), or
-    None when there is no measurement or the kernel source changed since it was taken."""
+    None when there is no measurement or the kernel's sources changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)[kernel]
-        if t.get("source_sha256") != source_digest(GEMM_SOURCE):
+        if t.get("source_sha256") != source_digest(KERNEL_SOURCES[kernel]):
             return None
         return int(t["bytes_per_launch"])
     except (OSError, ValueError, KeyError, TypeError):
@@ -106,7 +118,10 @@ def main():
     torch.cuda.set_device(dev)
     mxq.lib()
     if args.only:
-        only_quantize(args, torch, mxq, wl, dev)
+        if args.only.startswith("gemm"):
+            only_gemm(args, torch, mxq, wl, dev)
+        else:
+            only_quantize(args, torch, mxq, wl, dev)
         return
 
     d = wl.workload2()
@@ -479,6 +494,42 @@ def only_quantize(args, torch, mxq, wl, dev):
     print(json.dumps({"kernel": args.only, "workload": "[16384][16384] bf16, E4M3", "steps": args.steps,
                       "ms": round(ms, 5), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                       "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}))
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+
+
+def only_gemm(args, torch, mxq, wl, dev):
+    """One GEMM mode alone on the projection workload (codes quantized once, untimed):
+    bf16 output, W untimed launches then K timed ones."""
+    import ctypes
+    L = mxq.lib()
+    stream = torch.cuda.current_stream()
+    d = wl.workload2()
+    M, K, N = d["M"], d["K"], d["N"]
+    xc, xs = mxq.quantize(d["x"].to(dev), "e4m3", "row")
+    wc, ws = mxq.quantize(d["w"].to(dev), "e4m3", "row")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    acc = mxq.MXQ_ACC_FP32 if ONLY_KERNELS[args.only] == "exact" else mxq.MXQ_ACC_FP8_MFMA
+    a = (M, N, K, xc.data_ptr(), xc.stride(0), xs.data_ptr(), xs.stride(0), mxq.MXQ_E4M3, wc.data_ptr(), wc.stride(0),
+         ws.data_ptr(), ws.stride(0), mxq.MXQ_E4M3, ctypes.c_float(1.0), None, y.data_ptr(), mxq.MXQ_BF16, y.stride(0),
+         acc, ctypes.c_void_p(stream.cuda_stream))
+    st = L.mxq_gemm(*a)
+    if st != 0:
+        raise RuntimeError("%s failed: %s" % (args.only, mxq.mxq_status_string(st)))
+    for _ in range(args.warmup):
+        L.mxq_gemm(*a)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        L.mxq_gemm(*a)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    tflops = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+    print(json.dumps({"kernel": args.only, "workload": "projection M=%d K=%d N=%d, E4M3, bf16 out" % (M, K, N),
+                      "steps": args.steps, "ms": round(ms, 5), "tflops": round(tflops, 2),
+                      "frac_of_mxfp8_peak": round(tflops / PEAK_MXFP8_TFLOPS, 4),
+                      "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}))
     if args.copy_calibration:
         copy_calibration(torch, dev)
 

@@ -1,5 +1,5 @@
 """Host-side checks of bench.py's contract (no GPU): one GPU only, and the recorded HBM
-traffic is reported only for the GEMM source it was measured on."""
+traffic is reported only for the kernel sources it was measured on."""
 import json
 import os
 import subprocess
@@ -18,19 +18,22 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert r.stdout == ""
 
 
-def test_traffic_is_keyed_to_the_gemm_source(tmp_path, monkeypatch):
+def test_traffic_is_keyed_to_the_kernel_sources(tmp_path, monkeypatch):
     with open(bench.TRAFFIC_FILE) as f:
         recs = json.load(f)
     assert recs
     for key, rec in recs.items():
-        # the record's parts add up; it is reported exactly when it was taken on this source
+        # the record's parts add up; it is reported exactly when it was taken on these sources
         assert rec["bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
-        current = rec["source_sha256"] == bench.source_digest(bench.GEMM_SOURCE)
+        current = rec["source_sha256"] == bench.source_digest(bench.KERNEL_SOURCES[key])
         assert bench.load_traffic(key) == (rec["bytes_per_launch"] if current else None)
     # a changed source (or a missing record) reports no traffic
-    src = tmp_path / "gemm.hip"
-    src.write_bytes(open(bench.GEMM_SOURCE, "rb").read() + b"\n")
-    monkeypatch.setattr(bench, "GEMM_SOURCE", str(src))
+    sources = {}
+    for key, paths in bench.KERNEL_SOURCES.items():
+        src = tmp_path / (key + ".hip")
+        src.write_bytes(open(paths[0], "rb").read() + b"\n")
+        sources[key] = [str(src)] + paths[1:]
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", sources)
     for key in recs:
         assert bench.load_traffic(key) is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
