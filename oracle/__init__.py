@@ -49,8 +49,9 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build(force=False)
+        # (re)build when the library is missing or older than its source
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
         L = ctypes.CDLL(_LIB_PATH)
         u8p = ctypes.POINTER(ctypes.c_uint8)
         i64 = ctypes.c_int64
