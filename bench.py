@@ -59,14 +59,20 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true", help="also run a copy of known size (counter runs)")
     p.add_argument("--headline-only", action="store_true", help="time the step only (counter runs)")
     p.add_argument("--only", choices=sorted(ONLY_KERNELS), default=None,
-                   help="time one standalone quantize kernel on the 2^28 input alone (counter runs)")
+                   help="time one kernel alone: a quantize entry point on the 2^28 input, a GEMM mode on the "
+                        "projection, or a torch reference kernel (counter runs, ceilings)")
     return p.parse_args()
 
 
 # --only: one quantize entry point on the [16384][16384] bf16 input, E4M3, or one GEMM
 # mode on the projection workload
 ONLY_KERNELS = {"quantize_2p28": "rowwise", "quantize_2p28_colwise": "colwise", "quantize_2p28_dual": "dual",
-                "gemm_exact": "exact", "gemm_fp8": "fp8"}
+                "gemm_exact": "exact", "gemm_fp8": "fp8",
+                # practical ceilings on the same machine, from torch's own kernels (context only):
+                # an elementwise bf16 -> int8 cast and a bf16 copy of the 2^28 input (the byte mixes
+                # of one and two quantize orientations), and torch.mm on bf16 operands of the
+                # projection shape (the library GEMM on the matrix cores the exact mode uses)
+                "ref_cast_2p28": "ref_cast", "ref_copy_2p28": "ref_copy", "ref_mm_bf16": "ref_mm"}
 
 
 _CSRC = os.path.join(ROOT, "mxfp8_block_scaled_03_amd", "csrc")
@@ -118,7 +124,9 @@ def main():
     torch.cuda.set_device(dev)
     mxq.lib()
     if args.only:
-        if args.only.startswith("gemm"):
+        if args.only.startswith("ref_"):
+            only_reference(args, torch, wl, dev)
+        elif args.only.startswith("gemm"):
             only_gemm(args, torch, mxq, wl, dev)
         else:
             only_quantize(args, torch, mxq, wl, dev)
@@ -532,6 +540,45 @@ def only_gemm(args, torch, mxq, wl, dev):
                       "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}))
     if args.copy_calibration:
         copy_calibration(torch, dev)
+
+
+def only_reference(args, torch, wl, dev):
+    """torch's own kernels on the same shapes, timed like the --only legs: what a plain
+    streaming kernel (cast, copy) and the library bf16 GEMM reach on this machine."""
+    kind = ONLY_KERNELS[args.only]
+    if kind == "ref_mm":
+        d = wl.workload2()
+        M, K, N = d["M"], d["K"], d["N"]
+        xb = d["x"].to(dev)
+        wt = d["w"].to(dev).t().contiguous()          # [K][N]: a plain NN product
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        call = lambda: torch.mm(xb, wt, out=y)  # noqa: E731
+        work = 2.0 * M * N * K
+        what = "torch.mm bf16 [%d][%d] x [%d][%d], bf16 out" % (M, K, K, N)
+    else:
+        x = wl.workload_q()["x"].to(dev)
+        y = torch.empty(x.shape, dtype=torch.int8 if kind == "ref_cast" else torch.bfloat16, device=dev)
+        call = lambda: y.copy_(x)  # noqa: E731
+        work = x.numel() * (2 + y.element_size())
+        what = "[16384][16384] bf16 -> %s elementwise copy" % ("int8" if kind == "ref_cast" else "bf16")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup + 1):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    res = {"kernel": args.only, "workload": what, "steps": args.steps, "ms": round(ms, 5)}
+    if kind == "ref_mm":
+        tflops = work / (ms * 1e-3) / 1e12
+        res.update({"tflops": round(tflops, 2), "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)})
+    else:
+        gbs = work / (ms * 1e-3) / 1e9
+        res.update({"gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)})
+    print(json.dumps(res))
 
 
 def copy_calibration(torch, dev):

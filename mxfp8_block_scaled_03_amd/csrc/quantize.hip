@@ -486,17 +486,25 @@ __global__ __launch_bounds__(kThreads) void k_quant_dual_lds(const void* __restr
   const int row_bytes = (int)(ld_src * ES);
   const int chunk = tid & 15;
   const int64_t cc = c0 + 8 * chunk;               // first column of the lane's chunks
+  // every load of the tile is issued before the first store: the compiler cannot move a
+  // buffer load across the code stores, so loads interleaved with them would each wait a
+  // full memory round trip in turn
+  Chunk<SRC_BF16> chs[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int row = (tid >> 4) + 16 * q;
-    Chunk<SRC_BF16> ch;
 #pragma unroll
     for (int h = 0; h < ES / 2; ++h) {             // 16-byte pieces of the chunk
       const auto d = __builtin_amdgcn_raw_buffer_load_b128(rs, row * row_bytes + (8 * chunk) * ES + 16 * h, 0, 0);
       const bool in = cc + (16 / ES) * h < cols;   // pieces past cols are padding
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ch.w[4 * h + i] = in ? (uint32_t)d[i] : 0u;
+      for (int i = 0; i < 4; ++i) chs[q].w[4 * h + i] = in ? (uint32_t)d[i] : 0u;
     }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = (tid >> 4) + 16 * q;
+    const Chunk<SRC_BF16>& ch = chs[q];
     const int sw = SWZ * ((row >> 5) & 3);
 #pragma unroll
     for (int h = 0; h < ES / 2; ++h)
