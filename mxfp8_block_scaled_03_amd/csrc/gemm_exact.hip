@@ -29,8 +29,11 @@
 // Scale bytes travel the same way, 4 bytes (4 blocks) per row into a four-slot ring.
 // Each stage is four k16 steps; in step t the wave issues its 16 MFMAs on the bf16 operands
 // of step t while, between them, it converts the codes of step t + 1 (two conversions per
-// MFMA), reads the codes of the next block from LDS and issues its share of the DMA.  One
-// workgroup barrier per stage hands the stage ring over.
+// MFMA on average), reads the codes of the next block from LDS and issues its share of the
+// DMA.  The program order puts two conversions after each MFMA; inside a step the compiler
+// may regroup them (scheduling fences only at the step boundaries: it clusters up to seven
+// conversions behind some MFMAs and none behind others, which measured ~2 % faster than
+// the strict interleave).  One workgroup barrier per stage hands the stage ring over.
 //
 // Edges.  Rows past the matrix and K bytes past a row read as zero through the buffer
 // descriptor's bound; in the last stage the code bytes at k >= K are zeroed in LDS once, and
@@ -380,7 +383,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
         if (m >= 8) make_sf(2 * s + 1, m - 8);
         if ((m & 3) == 1) read_codes(2 * s + 1, 4 + (m >> 2));
         if (m == 3 || m == 8 || m == 13) dma_part(s - 1, m == 3 ? 6 : (m == 8 ? 7 : 8));
-        __builtin_amdgcn_sched_barrier(0);
       }
       // stage s+1 landed everywhere (19 loads were issued after its codes), and every wave
       // has finished reading stage s, whose slot the DMA of stage s+4 now reuses
@@ -403,7 +405,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
         if ((m & 1) == 0) read_scale(Pn, m >> 1);
         if ((m & 3) == 1) read_codes(2 * s + 2, m >> 2);
         if (m == 6 || m == 14) dma_part(s, m >> 3);
-        __builtin_amdgcn_sched_barrier(0);
       }
       fix_scale(Pn);
       // step 4s+2: convert block 2s+1 half 1; scale values of block 2s+2; frags 4..7 of
@@ -415,7 +416,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
         if (m >= 8) make_sf(2 * s + 2, m - 8);
         if ((m & 3) == 1) read_codes(2 * s + 2, 4 + (m >> 2));
         if (m == 6 || m == 14) dma_part(s, 2 + (m >> 3));
-        __builtin_amdgcn_sched_barrier(0);
       }
       // step 4s+3: convert block 2s+2 half 0; frags 0..3 of block 2s+3 (stage s+1; frags
       // 4..7 follow in step 4s+4); DMA loads 4, 5
@@ -425,7 +425,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
         convert(0, 2 * s + 2, 0, m);
         if ((m & 3) == 1) read_codes(2 * s + 3, m >> 2);
         if (m == 6 || m == 14) dma_part(s, 4 + (m >> 3));
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // loads 6..8 of the last iteration
