@@ -124,6 +124,27 @@ __device__ __forceinline__ float decode_fp8(uint32_t c) {
   return __uint_as_float(__float_as_uint(v) | sign);
 }
 
+// fp32 value 2^(byte-127) of an E8M0 scale byte: ldexp of the subnormal 2^-127 by the byte
+// (byte 0 stays 2^-127, byte 254 is 2^127, byte 255 gives +Inf), then v * 0 + v, which is v
+// for every finite v and NaN for +Inf: byte 255 is NaN, with no compare.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t byte) {
+  const float v = __builtin_amdgcn_ldexpf(__uint_as_float(0x00400000u), (int)byte);
+  return __builtin_fmaf(v, 0.0f, v);
+}
+
+// Two codes of a dword (bytes 2*hi, 2*hi+1) times the scale s = e8m0_to_f32(byte), as two
+// bf16 values (the dword's bits), by the format's scaled conversion
+// (v_cvt_scalef32_pk_bf16_{fp8,bf8}: for every code and scale byte, 255 and the subnormal
+// 2^-127 included, the bf16 RNE of the exact product code * 2^(byte-127), NaN for NaN).
+template <int F>
+__device__ __forceinline__ uint32_t cvt_pk_bf16(uint32_t codes, float s, bool hi) {
+  if (F == kE4M3)
+    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, s, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, s, false));
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(codes, s, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(codes, s, false));
+}
+
 // bf16 round-to-nearest-even of an fp32 value (NaN -> quiet NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

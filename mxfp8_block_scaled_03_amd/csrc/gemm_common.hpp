@@ -130,31 +130,13 @@ __device__ __forceinline__ v4i mask_bytes(v4i v, int lim) {
 }
 
 
-// fp32 value 2^(byte-127) of an E8M0 byte (byte 0 is the fp32 subnormal 2^-127; 255 NaN).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t byte) {
-  return __uint_as_float(byte == 0 ? 0x00400000u : (byte == 255 ? 0x7FC00000u : byte << 23));
-}
-
 // Eight codes (two dwords) -> eight bf16 values code * scale (exact while the product is
 // inside bf16's range), with the gfx950 scaled conversion.
 template <int F>
 __device__ __forceinline__ v8bf codes_to_bf16(uint32_t w0, uint32_t w1, float s) {
-  v2bf p0, p1, p2, p3;
-  if (F == kE4M3) {
-    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);
-    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true);
-    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false);
-    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true);
-  } else {
-    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, s, false);
-    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w0, s, true);
-    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, s, false);
-    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w1, s, true);
-  }
-  typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
-  v4bf lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
-  v4bf hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  const v4i d = {(int)cvt_pk_bf16<F>(w0, s, false), (int)cvt_pk_bf16<F>(w0, s, true),
+                 (int)cvt_pk_bf16<F>(w1, s, false), (int)cvt_pk_bf16<F>(w1, s, true)};
+  return __builtin_bit_cast(v8bf, d);
 }
 
 // Exact-product accumulation: each lane decodes its codes with their block scale into

@@ -83,25 +83,6 @@ __device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, v4i rsrc) {
 }
 #pragma clang diagnostic pop
 
-// fp32 value 2^(byte-127) of an E8M0 scale byte: ldexp of the subnormal 2^-127 by the byte
-// (byte 0 stays 2^-127, byte 254 is 2^127, byte 255 gives +Inf), then v * 0 + v, which is v
-// for every finite v and NaN for +Inf: byte 255 is NaN, with no compare.
-__device__ __forceinline__ float scale_f32(uint32_t byte) {
-  const float v = __builtin_amdgcn_ldexpf(__uint_as_float(0x00400000u), (int)byte);
-  return __builtin_fmaf(v, 0.0f, v);
-}
-
-// Two codes of a dword (bytes 2*hi, 2*hi+1) times the scale, as two bf16 values (the
-// dword's bits), by the format's scaled conversion.
-template <int F>
-__device__ __forceinline__ int cvt2(uint32_t codes, float s, bool hi) {
-  if (F == kE4M3)
-    return __builtin_bit_cast(int, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, s, true)
-                                      : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, s, false));
-  return __builtin_bit_cast(int, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(codes, s, true)
-                                    : __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(codes, s, false));
-}
-
 template <int FA, int FB>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, int tiles_m, int tiles_n,
                                                         const uint8_t* __restrict__ xc, int64_t ld_x,
@@ -269,7 +250,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     }
   };
   auto make_sf = [&](int b, int f) __attribute__((always_inline)) {
-    sf[b & 1][f] = scale_f32((sdw[f] >> (8 * (b & 3))) & 0xFFu);
+    sf[b & 1][f] = e8m0_to_f32((sdw[f] >> (8 * (b & 3))) & 0xFFu);
   };
   // conversion piece q (0..15) of a k16 step (block b, half h): frag q / 2, code dword
   // 2h + (q & 1) -> operand dwords 2(q & 1), 2(q & 1) + 1 of opd[o]
@@ -279,11 +260,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     const float s = sf[b & 1][f];
     int lo, hi;
     if (f < 4) {
-      lo = cvt2<FA>(src, s, false);
-      hi = cvt2<FA>(src, s, true);
+      lo = (int)cvt_pk_bf16<FA>(src, s, false);
+      hi = (int)cvt_pk_bf16<FA>(src, s, true);
     } else {
-      lo = cvt2<FB>(src, s, false);
-      hi = cvt2<FB>(src, s, true);
+      lo = (int)cvt_pk_bf16<FB>(src, s, false);
+      hi = (int)cvt_pk_bf16<FB>(src, s, true);
     }
     // keep the conversions in their slot (no pass may sink them towards their MFMAs)
     asm volatile("" : "+v"(lo), "+v"(hi));

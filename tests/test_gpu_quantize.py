@@ -349,6 +349,47 @@ def test_dequantize_exact(fmt, out, K):
         assert np.array_equal(a[~nan_r], ref[~nan_r])
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_dequantize_layouts(fmt, out):
+    """Leading dimensions through the C ABI: code rows holding only K bytes (the
+    element-wise path), padded code rows with an output row wider than K (the block path
+    with a partial last block: nothing is written past K), and a dense array of 2^20
+    elements (the flat block path); every element bitwise against the oracle."""
+    import ctypes
+    rng = np.random.default_rng(90)
+    es = 4 if out == torch.float32 else 2
+    wide = mxq.MXQ_F32 if out == torch.float32 else mxq.MXQ_BF16
+    for L, K, ld_c, ld_d in ((33, 40, 40, 40), (33, 40, 48, 48), (33, 40, 64, 48), (21, 100, 128, 104),
+                             (1024, 1024, 1024, 1024)):
+        say("dequantize layout %s %s L=%d K=%d ld_codes=%d ld_dst=%d" % (fmt, out, L, K, ld_c, ld_d))
+        nb = (K + 31) // 32
+        codes = rng.integers(0, 256, (L, ld_c)).astype(np.uint8)
+        scales = rng.integers(100, 160, (L, nb)).astype(np.uint8)
+        scales[0, 0], scales[-1, -1] = 255, 0
+        gc, gs = torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV)
+        canary = -7.0 if out == torch.float32 else -7.0
+        dst = torch.full((L, ld_d), canary, dtype=out, device=DEV)
+        st = mxq.mxq_dequantize(gc.data_ptr(), ld_c, gs.data_ptr(), nb, mxq.MXQ_E4M3 if fmt == "e4m3" else mxq.MXQ_E5M2,
+                                L, K, dst.data_ptr(), wide, ld_d, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+        torch.cuda.synchronize()
+        y = dst.cpu()
+        assert torch.all(y[:, K:] == canary), "write past K"
+        ref = oracle.dequantize(np.ascontiguousarray(codes[:, :K]), scales, fmt, K, "f32" if es == 4 else "bf16")
+        a = y[:, :K].contiguous()
+        if es == 4:
+            a = a.numpy()
+            assert np.array_equal(np.isnan(a), np.isnan(ref))
+            m = ~np.isnan(ref)
+            assert np.array_equal(a[m].view(np.uint32), ref[m].view(np.uint32))
+        else:
+            a = a.view(torch.int16).numpy().view(np.uint16)
+            nan_r = (ref & 0x7FFF) > 0x7F80
+            assert np.array_equal((a & 0x7FFF) > 0x7F80, nan_r)
+            assert np.array_equal(a[~nan_r], ref[~nan_r])
+
+
 def test_quantize_dequantize_roundtrip_two_row():
     from conftest import load_golden
     g = load_golden("two_row_projection.json")
