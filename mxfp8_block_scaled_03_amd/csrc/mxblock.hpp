@@ -266,11 +266,37 @@ __device__ __forceinline__ uint32_t encode_sr(uint32_t vb, uint32_t sb, uint32_t
   constexpr int MB = F == kE4M3 ? 3 : 2;            // mantissa bits
   constexpr int BIAS = F == kE4M3 ? 7 : 15;
   constexpr int EMIN = 1 - BIAS;                    // exponent of the smallest normal
+  constexpr int KB = 23 - MB;                       // fp32 mantissa bits below the code's
   const uint32_t sign = (vb >> 24) & 0x80u;
   const uint32_t mag = vb & 0x7FFFFFFFu;
-  if (mag == 0u) return sign;
   const int e = (int)sb - 127;
   const int ev0 = (int)(mag >> 23);
+  const int xa0 = ev0 - 127 - e;                    // floor(log2 |a|) for an fp32-normal v
+  // v an fp32 normal and a = v / S in FP8's normal range (the common case): the steps below
+  // with lz = 0 and sh = -KB, so the floor code is v's exponent rebased with its top MB
+  // mantissa bits, and the KB bits below them are the fraction: up iff r < frac * 2^(24 - KB)
+  if (ev0 != 0 && xa0 >= EMIN) {
+    const uint32_t fc = ((uint32_t)(xa0 + BIAS) << MB) | ((mag >> KB) & ((1u << MB) - 1u));
+    const uint32_t frac = mag & ((1u << KB) - 1u);
+    return sign | (fc + (r < (frac << (24 - KB)) ? 1u : 0u));
+  }
+  // v an fp32 normal with a below FP8's normal range (or zero, whose code is its sign):
+  // the subnormal spacing 2^(EMIN - MB), k = -sh > KB fraction bits, floor code M >> k
+  if (ev0 != 0 || mag == 0u) {
+    const uint32_t M = (mag & 0x7FFFFFu) | 0x800000u;
+    const int k = 150 + e + EMIN - MB - ev0;                   // fraction bits of q
+    const uint32_t fc = M >> (k < 31 ? k : 31);
+    // up iff r < p * 2^24: while k <= 24, p * 2^24 = frac * 2^(24 - k) with frac the low k
+    // bits of M; beyond, q < 1 and r < M / 2^(k - 24) iff r < ceil(M / 2^(k - 24)), which
+    // is 1 (r == 0) once k - 24 >= 24
+    const int k1 = k < 24 ? k : 24;
+    const uint32_t t_lo = (M & ((1u << k1) - 1u)) << (24 - k1);
+    const int kk = k - 24 < 24 ? k - 24 : 24;
+    const uint32_t t_hi = kk < 24 ? (M + (1u << (kk > 0 ? kk : 0)) - 1u) >> (kk > 0 ? kk : 0) : 1u;
+    const uint32_t up = r < (k <= 24 ? t_lo : t_hi) ? 1u : 0u;
+    return mag == 0u ? sign : sign | (fc + up);
+  }
+  // v an fp32 subnormal: the general steps
   const uint32_t M = ev0 ? ((mag & 0x7FFFFFu) | 0x800000u) : (mag & 0x7FFFFFu);
   const int ev = ev0 ? ev0 : 1;
   const int lz = __clz((int)M) - 8;                 // leading zeros within 24 bits
