@@ -268,12 +268,15 @@ struct CtGeom {
   static constexpr int SWZ = 2 * ES;                // dwords of a half-wave's 8 columns
 };
 
-template <int SRC_BF16, int F, int R>
+// SR: stochastically rounded codes (encode_sr with the block's Philox words, line col,
+// block b -> block index col * nb + b, as k_quant_cols_sr) under the RNE quantizer's scale.
+template <int SRC_BF16, int F, int R, bool SR>
 __global__ __launch_bounds__(kThreads) void k_quant_cols_lds(const void* __restrict__ src, int64_t rows,
                                                             int64_t cols, int64_t ld_src, int64_t nb,
                                                             uint8_t* __restrict__ codes, int64_t ld_codes,
                                                             uint8_t* __restrict__ scales, int64_t ld_scales,
-                                                            int64_t gx, int64_t ntiles, int64_t per_xcd) {
+                                                            int64_t gx, int64_t ntiles, int64_t per_xcd,
+                                                            uint64_t seed) {
   typedef CtGeom<SRC_BF16> G;
   __shared__ __align__(16) uint32_t ctile[128 * G::RW];
   const int tid = threadIdx.x;
@@ -326,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols_lds(const void* __restr
 #pragma unroll
     for (int i = 0; i < 32; ++i) m = pk_abs_max_bf16(m, w[i]);
     sb = scale_byte_rule<F, R>(m << 16);
-    encode_block32_bf16_half<F, R>(w, false, sb, c);
+    if (!SR) encode_block32_bf16_half<F, R>(w, false, sb, c);
   } else {
     uint32_t amax = 0;
 #pragma unroll
@@ -335,7 +338,26 @@ __global__ __launch_bounds__(kThreads) void k_quant_cols_lds(const void* __restr
       amax = amax > a ? amax : a;
     }
     sb = scale_byte_rule<F, R>(amax);
-    encode_block32<F, R>(w, sb, c);
+    if (!SR) encode_block32<F, R>(w, sb, c);
+  }
+  if (SR) {
+    if (sb == 255u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = 0x7F7F7F7Fu;
+    } else {
+      uint32_t rnd[32];
+      block_random24((uint64_t)col * (uint64_t)nb + (uint64_t)b, seed, rnd);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t cw = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t vb = SRC_BF16 ? w[4 * i + j] << 16 : w[4 * i + j];
+          cw |= encode_sr<F>(vb, sb, rnd[4 * i + j]) << (8 * j);
+        }
+        c[i] = cw;
+      }
+    }
   }
   uint4* dst = reinterpret_cast<uint4*>(codes + col * ld_codes + 32 * b);
   dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
@@ -891,8 +913,9 @@ static hipError_t quant_cols_t(const void* src, int64_t rows, int64_t cols, int6
     const int64_t ntiles = gx * ((rows + 127) / 128);
     const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
     if (kXcds * per_xcd > 0x7FFFFFFF) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_quant_cols_lds<SRC_BF16, F, R>), dim3((unsigned)(kXcds * per_xcd)), dim3(kThreads), 0,
-                       stream, src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales, gx, ntiles, per_xcd);
+    hipLaunchKernelGGL((k_quant_cols_lds<SRC_BF16, F, R, false>), dim3((unsigned)(kXcds * per_xcd)), dim3(kThreads),
+                       0, stream, src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales, gx, ntiles, per_xcd,
+                       (uint64_t)0);
     return hipGetLastError();
   }
   if (buf)
@@ -989,6 +1012,19 @@ static hipError_t quant_sr_t(const void* src, int64_t rows, int64_t cols, int64_
     return hipGetLastError();
   }
   const int64_t nb = (rows + 31) / 32;
+  constexpr int64_t ES = SRC_BF16 ? 2 : 4;
+  if ((uintptr_t)src % 16 == 0 && (ld_src * ES) % 16 == 0 && (cols * ES) % 16 == 0 &&
+      128 * ld_src * ES < ((int64_t)1 << 31)) {
+    // the columnwise LDS tile kernel of quant_cols_t with the stochastic encoder
+    const int64_t tgx = (cols + CtGeom<SRC_BF16>::TC - 1) / CtGeom<SRC_BF16>::TC;
+    const int64_t ntiles = tgx * ((rows + 127) / 128);
+    const int64_t per_xcd = (ntiles + kXcds - 1) / kXcds;
+    if (kXcds * per_xcd > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_quant_cols_lds<SRC_BF16, F, kRuleCeil, true>), dim3((unsigned)(kXcds * per_xcd)),
+                       dim3(kThreads), 0, stream, src, rows, cols, ld_src, nb, codes, ld_codes, scales, ld_scales,
+                       tgx, ntiles, per_xcd, seed);
+    return hipGetLastError();
+  }
   const int64_t gx = (cols + kColTileCols - 1) / kColTileCols;
   int64_t gy = (rows + kColTileRows - 1) / kColTileRows;
   if (gy > 65535) gy = 65535;
