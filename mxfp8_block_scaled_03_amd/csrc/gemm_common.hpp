@@ -179,9 +179,23 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
-// Round-to-nearest-even float -> bf16 bits of two values, packed (lo = a).
+// Buffer descriptor over an epilogue's bias array (4 * n bytes; range 0 without a bias, so
+// every load through it returns zeros without touching memory; kNoBias is then its base).
+__device__ const float kNoBias = -0.0f;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bias_rsrc(const float* bias, int n) {
+  const int64_t bytes = bias != nullptr ? 4 * (int64_t)n : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(bias != nullptr ? bias : &kNoBias), (short)0,
+                                           (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF), 0x00020000);
+}
+
+// Round-to-nearest-even float -> bf16 bits of two values, packed (lo = a), by the
+// hardware conversion v_cvt_pk_bf16_f32 (the bits of f32_to_bf16_rne for every non-NaN
+// value, subnormals included; NaN stays a NaN).
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return f32_to_bf16_rne(a) | (f32_to_bf16_rne(b) << 16);
+  typedef float v2f_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  const v2f_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2bf_t));
 }
 
 }  // namespace

@@ -372,7 +372,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
   //      wave's 128x64 block).
   const int wrow0 = m0 + gp * 128, wcol0 = n0 + wq * 64;
   {
+    // branch free: the lane's 32 bias values, four consecutive columns per (fj, q), come
+    // through the bias descriptor; the addend is -0 without a bias or past N (x + -0 == x
+    // for every x, -0 included)
     const bool has_bias = ep.bias != nullptr;
+    const __amdgpu_buffer_rsrc_t brs = bias_rsrc(ep.bias, N);
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    v4f bq[2][4];
+#pragma unroll
+    for (int fj = 0; fj < 2; ++fj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        bq[fj][q] = __builtin_bit_cast(
+            v4f, __builtin_amdgcn_raw_buffer_load_b128(brs, 4 * (wcol0 + 32 * fj + 8 * q + 4 * lg), 0, 0));
 #pragma unroll
     for (int fj = 0; fj < 2; ++fj)
 #pragma unroll
@@ -380,12 +392,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pp(int M, int N, int K, in
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int col = wcol0 + 32 * fj + 8 * q + 4 * lg + e;
-          const float bv = (has_bias && col < N) ? ep.bias[col] : 0.0f;
+          const float bv = (has_bias && col < N) ? bq[fj][q][e] : -0.0f;
 #pragma unroll
-          for (int fi = 0; fi < 4; ++fi) {
-            const float a = acc[fi][fj][4 * q + e];
-            acc[fi][fj][4 * q + e] = has_bias ? __builtin_fmaf(ep.alpha, a, bv) : ep.alpha * a;
-          }
+          for (int fi = 0; fi < 4; ++fi)
+            acc[fi][fj][4 * q + e] = __builtin_fmaf(ep.alpha, acc[fi][fj][4 * q + e], bv);
         }
     if (ep.act) {
 #pragma unroll
