@@ -65,6 +65,26 @@ def test_gemm_epilogue(out, alpha, bias, accum):
     run_case(270, 300, 352, out=out, alpha=alpha, bias=bias, seed=2, what="epilogue", accum=accum)
 
 
+@pytest.mark.parametrize("accum", ACCS)
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_gemm_bias_view_unaligned(out, accum):
+    """The epilogue reads the bias four columns at a time through a buffer descriptor: a
+    bias starting one float into its buffer (4-byte, not 16-byte aligned) and N not a
+    multiple of 4 give the same per-element parity."""
+    say("gemm unaligned bias view %s accum %s" % (out, accum))
+    M, N, K = 300, 301, 352
+    rng = np.random.default_rng(21)
+    xc, xs = quantized(rng, M, K, 1.0, "e4m3")
+    wc, ws = quantized(rng, N, K, 0.02, "e4m3")
+    big = torch.from_numpy(rng.standard_normal(N + 7).astype(np.float32) * 0.5).to(DEV)
+    b = big[1:N + 1]
+    assert b.data_ptr() % 16 == 4
+    y = mxq.gemm(xc, xs, wc, ws, K, alpha=-0.75, bias=b, out_dtype=out, accum=accum)
+    torch.cuda.synchronize()
+    full_check(xc, xs, "e4m3", wc, ws, "e4m3", K, y, out, alpha=-0.75, bias=b, what="%s unaligned bias" % accum,
+               strict=accum == "fp32")
+
+
 def test_gemm_k_zero_writes_bias():
     rng = np.random.default_rng(3)
     b = torch.from_numpy(rng.standard_normal(50).astype(np.float32)).to(DEV)
