@@ -72,15 +72,15 @@ __device__ __forceinline__ float silu(float x) {
 
 
 // MX-quantize a wave's block of bf16 output values staged in LDS, along its rows: 128 rows
-// of 32 * NB values at LDS offset `base`, row pitch 64 * NB bytes, 16-byte chunk c of row r
+// of 32 * NB values at LDS offset `base`, row pitch PITCH bytes, 16-byte chunk c of row r
 // stored at chunk c ^ (r & 7), values past column N staged as +0 (the zero padding of a
 // partial block).  Row r, block j becomes block blk0 + j of code row row0 + r ("Microscaling:
 // the two-row experiment": amax, power-of-two scale, RNE codes), written only when the row
 // is < M and the block < nbq.
-template <int NB>
+template <int NB, int PITCH = 64 * NB>
 __device__ __forceinline__ void quantize_staged(uint32_t base, int lane, int row0, int M, int blk0, int nbq,
                                                 const GemmEpilogue& ep) {
-  constexpr int PITCH = 64 * NB;
+  static_assert(PITCH >= 64 * NB && PITCH % 128 == 0, "staged row pitch");
 #pragma unroll 1
   for (int it = 0; it < 2 * NB; ++it) {
     const int p = 64 * it + lane, r = p / NB, j = p % NB;

@@ -17,7 +17,9 @@
 //
 // Work split.  256x256 output tile per workgroup of 4 waves, one wave per SIMD; wave
 // (wm, wn) owns the 128x128 block of X rows 128 wm.. and W rows 128 wn.. (4x4 MFMA tiles,
-// 256 FP32 accumulators per lane).  A wave decodes each of its 256 fragment rows once per
+// 256 FP32 accumulators per lane).  A narrow variant (256x192 tile, 128x96 per wave, 4x3
+// MFMA tiles) runs the same loop without the fourth W fragment column; it is chosen on the
+// host where its rounds fill the CUs better.  A wave decodes each of its 256 fragment rows once per
 // K element: two conversion instructions per MFMA, which the matrix core's 32-cycle issue
 // interval hides.
 //
@@ -40,7 +42,12 @@
 // a block past nb gets scale byte 127 there (1.0: its zero codes then contribute exactly
 // zero whatever byte the caller's array holds past the end).  Scale rows
 // are read in 4-byte words; the last row of X or W, whose final word may end past the
-// caller's array, has its last partial word read byte by byte instead.
+// caller's array, has its last partial word read byte by byte instead.  The narrow tile
+// keeps the stage layout of 256 W rows: its descriptor ends at its 192 rows, so the DMA of
+// rows 192..255 lands zeros that no fragment reads.
+#include <cstdlib>
+#include <cstring>
+
 #include "gemm_common.hpp"
 
 namespace mxq {
@@ -83,13 +90,16 @@ __device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, v4i rsrc) {
 }
 #pragma clang diagnostic pop
 
-template <int FA, int FB>
+template <int FA, int FB, int BNT>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, int tiles_m, int tiles_n,
                                                         const uint8_t* __restrict__ xc, int64_t ld_x,
                                                         const uint8_t* __restrict__ xs, int64_t ld_xs,
                                                         const uint8_t* __restrict__ wc, int64_t ld_w,
                                                         const uint8_t* __restrict__ ws, int64_t ld_ws,
                                                         const GemmEpilogue ep, const ExSplit sp) {
+  static_assert(BNT == 256 || BNT == 192, "tile width");
+  constexpr int WN = BNT / 2;               // output columns (W rows) per wave
+  constexpr int NFW = WN / 32;              // W fragments per wave
   // work item -> tile and K-stage range [s0, s0 + S); the fix-up launch takes tile
   // full + blockIdx.x and no stages
   const int S_all = (K + 63) / 64;          // stages of the whole K
@@ -109,7 +119,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   const int S = sp.fix ? 0 : (half == 0 ? sp.s_half : S_all - s0);   // stages of this item
   const int P0 = s0 >> 1;                   // its first scale word (s_half is even)
   const bool last_range = half != 0;        // holds the last stage
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * BNT;
   const int lane = threadIdx.x & 63;
   // the fix-up launch runs one wave per workgroup (4 per tile): its wave index comes from
   // the workgroup index, and its epilogue staging uses LDS slot 0
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   const int nb = (K + 31) / 32;             // blocks per line
   const int Kp = 32 * nb;
   const int nbf = nb / 4;                   // whole 4-block scale words per row
-  const int rows_x = min(BM, M - m0), rows_w = min(BN, N - n0);
+  const int rows_x = min(BM, M - m0), rows_w = min(BNT, N - n0);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
 
   // ---- code DMA: wave w loads rows 64w..64w+63 of both operands, 16 rows per load: lane
@@ -150,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   const bool s_is_x = wid < 2;
   const int s_rows = s_is_x ? rows_x : rows_w;
   const int64_t ld_s = s_is_x ? ld_xs : ld_ws;
-  const bool s_last_tile = s_is_x ? (m0 + BM >= M) : (n0 + BN >= N);
+  const bool s_last_tile = s_is_x ? (m0 + BM >= M) : (n0 + BNT >= N);
   const uint64_t s_base = (uint64_t)(uintptr_t)(s_is_x ? xs + (int64_t)m0 * ld_xs : ws + (int64_t)n0 * ld_ws);
   const uint32_t s_rowspan = (uint32_t)((int64_t)(s_rows - 1) * ld_s);
   const int s_words = s_last_tile ? nbf : (nb + 3) / 4;        // words of the descriptor's last row
@@ -191,20 +201,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     for (int e = 0; e < 2; ++e) {
       const uint32_t c = (uint32_t)(2 * e + lg);
       fx[e] = (uint32_t)(128 * wm + li) * 64u + ((c ^ sw) << 4);
-      fw[e] = (uint32_t)kOpBytes + (uint32_t)(128 * wn + li) * 64u + ((c ^ sw) << 4);
+      fw[e] = (uint32_t)kOpBytes + (uint32_t)(WN * wn + li) * 64u + ((c ^ sw) << 4);
     }
   }
   const uint32_t sx_rd = (uint32_t)kOffScale + (uint32_t)(128 * wm + li) * 4u;
-  const uint32_t sw_rd = (uint32_t)kOffScale + (uint32_t)(256 + 128 * wn + li) * 4u;
+  const uint32_t sw_rd = (uint32_t)kOffScale + (uint32_t)(256 + WN * wn + li) * 4u;
 
   // ---- the last row's partial scale word (nb % 4 != 0), read byte by byte: of a lane's 4
   //      X (W) fragment rows, 32 apart, at most one is the last row of X (W)
   uint32_t tail_x = 0, tail_w = 0;
   int tail_fx = -1, tail_fw = -1;
   if ((nb & 3) != 0) {
-    const int rx = M - 1 - (m0 + 128 * wm + li), rw = N - 1 - (n0 + 128 * wn + li);
+    const int rx = M - 1 - (m0 + 128 * wm + li), rw = N - 1 - (n0 + WN * wn + li);
     if (rx >= 0 && rx < 128 && (rx & 31) == 0) tail_fx = rx >> 5;
-    if (rw >= 0 && rw < 128 && (rw & 31) == 0) tail_fw = rw >> 5;
+    if (rw >= 0 && rw < WN && (rw & 31) == 0) tail_fw = rw >> 5;
     if (tail_fx >= 0) {
       const uint8_t* p = xs + (int64_t)(M - 1) * ld_xs + 4 * nbf;
       for (int t = 0; t < (nb & 3); ++t) tail_x |= (uint32_t)p[t] << (8 * t);
@@ -230,11 +240,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   float sf[2][8];     // scale values of one block [block parity][frag]
 
   auto read_codes = [&](int b, int f) __attribute__((always_inline)) {
+    if (f >= 4 + NFW) return;
     const uint32_t so = (uint32_t)((b >> 1) & 3) * kStageBytes;
     const int e = b & 1;
     code[e][f] = f < 4 ? lds16(fx[e] + so, 2048 * f) : lds16(fw[e] + so, 2048 * (f - 4));
   };
   auto read_scale = [&](int P, int f) __attribute__((always_inline)) {
+    if (f >= 4 + NFW) return;
     const uint32_t sl = (uint32_t)(P & 3) * kScaleSlotBytes;
     const uint32_t a = (f < 4 ? sx_rd + 128u * (uint32_t)f : sw_rd + 128u * (uint32_t)(f - 4)) + sl;
     sdw[f] = *reinterpret_cast<const uint32_t*>(smem + a);
@@ -246,16 +258,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       sdw[f] = (last_word && tail_fx == f) ? tail_x : sdw[f];
-      sdw[4 + f] = (last_word && tail_fw == f) ? tail_w : sdw[4 + f];
+      if (f < NFW) sdw[4 + f] = (last_word && tail_fw == f) ? tail_w : sdw[4 + f];
     }
   };
   auto make_sf = [&](int b, int f) __attribute__((always_inline)) {
+    if (f >= 4 + NFW) return;
     sf[b & 1][f] = e8m0_to_f32((sdw[f] >> (8 * (b & 3))) & 0xFFu);
   };
   // conversion piece q (0..15) of a k16 step (block b, half h): frag q / 2, code dword
   // 2h + (q & 1) -> operand dwords 2(q & 1), 2(q & 1) + 1 of opd[o]
   auto convert = [&](int o, int b, int h, int q) __attribute__((always_inline)) {
     const int f = q >> 1, w = q & 1;
+    if (f >= 4 + NFW) return;
     const uint32_t src = (uint32_t)code[b & 1][f][2 * h + w];
     const float s = sf[b & 1][f];
     int lo, hi;
@@ -273,6 +287,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   };
   auto mfma = [&](int o, int m) __attribute__((always_inline)) {
     const int fi = m >> 2, fj = m & 3;
+    if (fj >= NFW) return;
     acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, opd[o][4 + fj]),
                                                           __builtin_bit_cast(v8bf, opd[o][fi]), acc[fi][fj], 0, 0, 0);
   };
@@ -415,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     wait_vm<0>();
     lds_barrier();
   }
-  if (sp.fix) {
+  if (BNT == 256 && sp.fix) {
     // the two K halves of the tile, row-major 256 x 256 FP32 in the workspace: their sums
     // added (the order of two addends does not change an FP32 sum)
     const float* p0 = sp.part + (int64_t)(2 * (t - sp.full)) * kPartFloats;
@@ -437,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   // no bias, activation or codes, fp32 rows of 256 into its slot of the workspace
   GemmEpilogue epx = ep;
   int Mx = M, Nx = N, m0x = m0, n0x = n0;
-  if (half >= 0) {
+  if (BNT == 256 && half >= 0) {
     epx.alpha = 1.0f;
     epx.bias = nullptr;
     epx.act = 0;
@@ -454,7 +469,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   // ---- epilogue: v = act(alpha * acc + bias[col]) in place.  Lane (g, i) holds
   //      Y[row 32 fi + i][col 32 fj + 8 q + 4 g + e] in acc[fi][fj][4 q + e], rows and
   //      columns relative to the wave's 128x128 block.
-  const int wrow0 = m0x + 128 * wm, wcol0 = n0x + 128 * wn;
+  const int wrow0 = m0x + 128 * wm, wcol0 = n0x + WN * wn;
   {
     // branch free: the lane's 64 bias values, four consecutive columns per (fj, q), come
     // through the bias descriptor; the addend is -0 without a bias or past N (x + -0 == x
@@ -462,15 +477,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     const bool has_bias = epx.bias != nullptr;
     const __amdgpu_buffer_rsrc_t brs = bias_rsrc(epx.bias, Nx);
     typedef float v4f __attribute__((ext_vector_type(4)));
-    v4f bq[4][4];
+    v4f bq[NFW][4];
 #pragma unroll
-    for (int fj = 0; fj < 4; ++fj)
+    for (int fj = 0; fj < NFW; ++fj)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         bq[fj][q] = __builtin_bit_cast(
             v4f, __builtin_amdgcn_raw_buffer_load_b128(brs, 4 * (wcol0 + 32 * fj + 8 * q + 4 * lg), 0, 0));
 #pragma unroll
-    for (int fj = 0; fj < 4; ++fj)
+    for (int fj = 0; fj < NFW; ++fj)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -485,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
 #pragma unroll
       for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
-        for (int fj = 0; fj < 4; ++fj)
+        for (int fj = 0; fj < NFW; ++fj)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[fi][fj][r] = silu(acc[fi][fj][r]);
     }
@@ -496,17 +511,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   };
-  // stage columns [64 P .. 64 P + 64 * W) of the wave's block as 128 rows of 256 bytes, 16-byte
-  // chunk c of row r at chunk c ^ (r & 7); bf16 (E = 2, all 128 columns) or fp32 (E = 4, 64
-  // columns per pass); columns >= N are staged as +0 when zero_past_n
+  // stage columns of the wave's block as 128 rows of 256 bytes, 16-byte chunk c of row r at
+  // chunk c ^ (r & 7); bf16 (E = 2, all WN columns) or fp32 (E = 4, columns 64 P .. 64 P + 63
+  // of pass P); columns >= N are staged as +0 when zero_past_n
   auto stage_rows = [&](auto e_c, int pass, bool zero_past_n) __attribute__((always_inline)) {
     constexpr int E = decltype(e_c)::value;
-    constexpr int FJN = E == 2 ? 4 : 2;
+    constexpr int FJN = E == 2 ? NFW : 2;
 #pragma unroll
     for (int fjl = 0; fjl < FJN; ++fjl)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int fj = pass * FJN + fjl;
+        if (fj >= NFW) continue;
         const int c0 = 32 * fjl + 8 * q + 4 * lg;           // first of this lane's 4 staged columns
         bool in[4];
 #pragma unroll
@@ -536,20 +552,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
       }
   };
   if (!epx.y) {
-  } else if (epx.y_vec16 && m0x + BM <= Mx && n0x + BN <= Nx) {
+  } else if (epx.y_vec16 && m0x + BM <= Mx && n0x + BNT <= Nx) {
     // interior tile, aligned y: staged rows stored as whole 16-byte pieces
     auto store_pass = [&](auto e_c, int pass) __attribute__((always_inline)) {
       constexpr int E = decltype(e_c)::value;
+      // 16-byte chunks per staged row in this pass
+      const int chunks = E == 2 ? WN / 8 : (min(64, WN - 64 * pass) * 4) / 16;
       stage_rows(e_c, pass, false);
       wave_lds_sync();
 #pragma unroll
       for (int it = 0; it < 32; ++it) {
         const int row = 4 * it + (lane >> 4), c = lane & 15;
-        const v4i v = *reinterpret_cast<const v4i*>(smem + wbase + (uint32_t)row * 256u +
-                                                    ((uint32_t)(c ^ (row & 7)) << 4));
-        uint8_t* dst = reinterpret_cast<uint8_t*>(epx.y) +
-                       ((int64_t)(wrow0 + row) * epx.ld_y + wcol0 + (E == 2 ? 0 : 64 * pass)) * E + 16 * c;
-        *reinterpret_cast<v4i*>(dst) = v;
+        if (c < chunks) {
+          const v4i v = *reinterpret_cast<const v4i*>(smem + wbase + (uint32_t)row * 256u +
+                                                      ((uint32_t)(c ^ (row & 7)) << 4));
+          uint8_t* dst = reinterpret_cast<uint8_t*>(epx.y) +
+                         ((int64_t)(wrow0 + row) * epx.ld_y + wcol0 + (E == 2 ? 0 : 64 * pass)) * E + 16 * c;
+          *reinterpret_cast<v4i*>(dst) = v;
+        }
       }
       wave_lds_sync();
     };
@@ -561,7 +581,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     }
   } else {
 #pragma unroll
-    for (int fj = 0; fj < 4; ++fj)
+    for (int fj = 0; fj < NFW; ++fj)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -585,7 +605,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     // then quantized along the rows in 32-column blocks
     stage_rows(std::integral_constant<int, 2>(), 0, true);
     wave_lds_sync();
-    quantize_staged<4>(wbase, lane, wrow0, Mx, wcol0 / 32, (Nx + 31) / 32, epx);
+    quantize_staged<NFW, 256>(wbase, lane, wrow0, Mx, wcol0 / 32, (Nx + 31) / 32, epx);
   }
 }
 
@@ -640,12 +660,41 @@ ExSplit plan_split(int64_t tiles, int64_t K, int cus) {
   return sp;
 }
 
-template <int FA, int FB>
+// Tile width for an M x N x K problem on `cus` CUs, from an estimate of each plan's time in
+// stage times of a full-width tile: a round of full-width tiles costs the S stages of K
+// plus a fixed part (prologue, epilogue, launch: about 8.5 stage times); the K split makes
+// a last round at most half full cost half a round plus a fix-up launch and a workspace; a
+// round of 256 x 192 tiles (3/4 of the work) measured 0.83 of a full-width round.  The
+// narrow tile wins where it fills its rounds better (4096 x 6144: 512 narrow tiles in two
+// full rounds against 384 wide ones in one and a half).  Problems of one round keep the
+// full width: there the fixed part dominates, and a narrow tile column of the edge would
+// take the per-element epilogue.  MXQ_EXACT_TILE_N=256 or 192 in the environment forces a
+// width.
+constexpr double kRoundFixed = 8.5, kNarrowCost = 0.83, kSplitFixed = 5.0, kFixupPerTile = 0.1;
+
+int choose_tile_n(int64_t M, int64_t N, int64_t K, int cus) {
+  if (const char* e = getenv("MXQ_EXACT_TILE_N")) {
+    if (strcmp(e, "192") == 0) return 192;
+    if (strcmp(e, "256") == 0) return 256;
+  }
+  const int64_t P = cus > 0 ? cus : 1, S = (K + 63) / 64, tm = (M + BM - 1) / BM;
+  const int64_t T256 = tm * ((N + 255) / 256), T192 = tm * ((N + 191) / 192);
+  if (T256 <= P) return 256;
+  const double round = (double)S + kRoundFixed;
+  const ExSplit sp = plan_split(T256, K, cus);
+  const double wide = sp.halves > 0 ? (double)(sp.full / P) * round + (double)(S / 2) + kRoundFixed + kSplitFixed +
+                                          kFixupPerTile * (double)(sp.halves / 2)
+                                    : (double)((T256 + P - 1) / P) * round;
+  const double narrow = (double)((T192 + P - 1) / P) * kNarrowCost * round;
+  return narrow < wide ? 192 : 256;
+}
+
+template <int FA, int FB, int BNT>
 hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
                     int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
                     const GemmEpilogue& ep, const ExSplit& sp, hipStream_t stream) {
   static bool attr_set[64] = {false};
-  auto kern = k_gemm_ex<FA, FB>;
+  auto kern = k_gemm_ex<FA, FB, BNT>;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (!attr_set[dev]) {
@@ -653,7 +702,7 @@ hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t 
     if (e != hipSuccess) return e;
     attr_set[dev] = true;
   }
-  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BNT - 1) / BNT);
   hipLaunchKernelGGL(kern, dim3(sp.full + sp.halves), dim3(kThreads), kLdsBytes, stream, (int)M, (int)N, (int)K,
                      tiles_m, tiles_n, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp);
   hipError_t e = hipGetLastError();
@@ -674,12 +723,26 @@ hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t 
   return hipGetLastError();
 }
 
+template <int FA, int FB>
+hipError_t launch_w(int bn, int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
+                    int64_t ld_xs, const uint8_t* wc, int64_t ld_w, const uint8_t* ws, int64_t ld_ws,
+                    const GemmEpilogue& ep, const ExSplit& sp, hipStream_t stream) {
+  if (bn == 192) return launch_f<FA, FB, 192>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
+  return launch_f<FA, FB, 256>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
+}
+
+// The split plan of the chosen width: the K split exists for full-width tiles only.
+ExSplit plan_for(int bn, int64_t M, int64_t N, int64_t K, int cus) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + bn - 1) / bn);
+  return plan_split(tiles, K, bn == 256 ? cus : 0);
+}
+
 }  // namespace ex
 }  // namespace
 
 int64_t gemm_exact_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + ex::BM - 1) / ex::BM) * ((N + ex::BN - 1) / ex::BN);
-  const ex::ExSplit sp = ex::plan_split(tiles, K, device_cu_count());
+  const int cus = device_cu_count();
+  const ex::ExSplit sp = ex::plan_for(ex::choose_tile_n(M, N, K, cus), M, N, K, cus);
   return (int64_t)sp.halves * ex::kPartFloats * (int64_t)sizeof(float);
 }
 
@@ -687,19 +750,20 @@ hipError_t launch_gemm_exact(int64_t M, int64_t N, int64_t K, const uint8_t* xc,
                              int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws,
                              int64_t ld_ws, int w_fmt, const GemmEpilogue& ep, void* workspace,
                              int64_t workspace_bytes, hipStream_t stream) {
-  const int64_t tiles = ((M + ex::BM - 1) / ex::BM) * ((N + ex::BN - 1) / ex::BN);
-  ex::ExSplit sp = ex::plan_split(tiles, K, device_cu_count());
+  const int cus = device_cu_count();
+  const int bn = ex::choose_tile_n(M, N, K, cus);
+  ex::ExSplit sp = ex::plan_for(bn, M, N, K, cus);
   if (sp.halves > 0) {
     if (workspace == nullptr || workspace_bytes < (int64_t)sp.halves * ex::kPartFloats * (int64_t)sizeof(float))
-      sp = ex::plan_split(tiles, K, 0);       // no room: the whole tiles only
+      sp = ex::plan_for(bn, M, N, K, 0);      // no room: the whole tiles only
     else
       sp.part = static_cast<float*>(workspace);
   }
   if (x_fmt == kE4M3 && w_fmt == kE4M3)
-    return ex::launch_f<0, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
-  if (x_fmt == kE4M3) return ex::launch_f<0, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
-  if (w_fmt == kE4M3) return ex::launch_f<1, 0>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
-  return ex::launch_f<1, 1>(M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
+    return ex::launch_w<0, 0>(bn, M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
+  if (x_fmt == kE4M3) return ex::launch_w<0, 1>(bn, M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
+  if (w_fmt == kE4M3) return ex::launch_w<1, 0>(bn, M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
+  return ex::launch_w<1, 1>(bn, M, N, K, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp, stream);
 }
 
 }  // namespace mxq

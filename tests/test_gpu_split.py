@@ -13,6 +13,13 @@ from gpu_helpers import check_gemm, host_src, say
 
 pytestmark = pytest.mark.gpu
 
+
+@pytest.fixture(autouse=True)
+def full_width_tiles(monkeypatch):
+    """The K split exists for 256 x 256 tiles only: keep the library from picking the
+    256 x 192 tile for these shapes."""
+    monkeypatch.setenv("MXQ_EXACT_TILE_N", "256")
+
 DEV = "cuda:0"
 TILE = 256
 
