@@ -81,7 +81,7 @@ KERNEL_SOURCES = {
     "gemm_exact": [os.path.join(_CSRC, "gemm_exact.hip"), os.path.join(_CSRC, "gemm_common.hpp")],
     "gemm_fp8": [os.path.join(_CSRC, "gemm_fp8.hip"), os.path.join(_CSRC, "gemm_common.hpp")],
 }
-GEMM_KERNEL_NAME = "mxq gemm, exact-product mode (ex::k_gemm_ex<0,0>: codes decoded to bf16 in registers, bf16 matrix cores)"
+GEMM_KERNEL_NAME = "mxq gemm, exact-product mode (ex::k_gemm_ex<0,0,256>: codes decoded to bf16 in registers, bf16 matrix cores)"
 FP8_LABEL = "FP8 matrix cores, 8-product groups truncated ~13 bits below their largest (outside 1e-5*T)"
 
 
