@@ -48,6 +48,20 @@ def accum_of(path):
     return "fp32" if path.endswith("exact") else "fp8"
 
 
+@pytest.fixture(params=["default", "192"], autouse=True)
+def tile_width(request, monkeypatch):
+    """Every exact-product test runs twice: with the tile width the library picks and with
+    the 256 x 192 tile forced (the FP8 path has one width, so its second run is skipped)."""
+    params = request.node.callspec.params if hasattr(request.node, "callspec") else {}
+    if request.param == "192":
+        fp8_only = request.node.originalname in ("test_fused_quant_respects_pitches_and_padding",
+                                                 "test_ffn_pair_full_size_with_fused_quant")
+        if fp8_only or (accum_of(params["path"]) if "path" in params else None) == "fp8":
+            pytest.skip("the tile width applies to the exact-product mode")
+        monkeypatch.setenv("MXQ_EXACT_TILE_N", "192")
+    return request.param
+
+
 @pytest.mark.parametrize("path", PATHS)
 def test_silu_epilogue_matches_oracle_silu(path):
     """Same accumulation with and without the activation (the GEMM is deterministic):

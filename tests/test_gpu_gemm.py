@@ -27,6 +27,18 @@ def quantized(rng, rows, K, std, fmt):
 ACCS = ["fp8", "fp32"]
 
 
+@pytest.fixture(params=["default", "192"], autouse=True)
+def tile_width(request, monkeypatch):
+    """Every exact-product test runs twice: with the tile width the library picks and with
+    the 256 x 192 tile forced (the FP8 path has one width, so its second run is skipped)."""
+    params = request.node.callspec.params if hasattr(request.node, "callspec") else {}
+    if request.param == "192":
+        if params.get("accum") == "fp8":
+            pytest.skip("the tile width applies to the exact-product mode")
+        monkeypatch.setenv("MXQ_EXACT_TILE_N", "192")
+    return request.param
+
+
 def run_case(M, N, K, fx="e4m3", fw="e4m3", out=torch.float32, alpha=1.0, bias=False, seed=0, xstd=1.0,
              what="", accum="fp8"):
     rng = np.random.default_rng(seed)
