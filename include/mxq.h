@@ -304,13 +304,16 @@ typedef enum { MXQ_ACT_NONE = 0, MXQ_ACT_SILU = 1 } mxq_act;
  * Tile rounds (MXQ_ACC_FP32 with 4-byte aligned scale rows).  The output is computed in
  * 256 x 256 or 256 x 192 tiles, one per CU at a time; the width is chosen per call from
  * an estimate of the rounds each needs (the environment variable MXQ_EXACT_TILE_N = 256
- * or 192 forces it).  Both widths give identical bits.  With 256 x 256 tiles, when there
- * are more tiles than CUs and the last round holds at most half as many tiles as there
- * are CUs, each of those tiles is computed as two halves of the K range, whose FP32 sums
- * are added (FP32) before the epilogue: the result stays within the same bound and is
- * deterministic for a given device, but its rounding differs from the unsplit order.
- * The halves' sums go to a workspace of 256 KiB per half tile, taken from the
- * stream-ordered pool for the call; if that allocation fails the tiles run whole.
+ * or 192 forces it).  Tiles computed whole give identical bits at either width.  With
+ * 256 x 256 tiles the K range of a tile may be split: when there are more tiles than
+ * CUs and the last round holds at most half as many tiles as there are CUs, each of
+ * those tiles is computed as two halves of K; when there are at most half as many tiles
+ * as CUs, every tile is computed as up to 16 K ranges.  The ranges' FP32 sums are added
+ * (FP32, in range order) before the epilogue: the result stays within the same bound and
+ * is deterministic for a given device, but its rounding differs from the unsplit order.
+ * The ranges' sums go to a workspace of 256 KiB per range, taken from the stream-ordered
+ * pool for the call; if that allocation fails the tiles run whole.  MXQ_EXACT_KSPLIT=0
+ * in the environment turns the split off.
  */
 int mxq_gemm_ex(int64_t M, int64_t N, int64_t K,
                 const uint8_t* x_codes, int64_t ld_x, const uint8_t* x_scales, int64_t ld_xs, int x_elem,

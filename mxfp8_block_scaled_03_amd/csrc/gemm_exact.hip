@@ -66,15 +66,15 @@ constexpr int kLdsBytes = kOffScale + kScaleSlots * kScaleSlotBytes;   // 136 Ki
 constexpr int kEpiWaveBytes = 32768;                 // per-wave epilogue staging (in the code stages)
 constexpr int kPartFloats = 4 * 64 * 256;            // one tile's FP32 accumulators (256 KiB)
 
-// K split of the last round's tiles.  Items 0 .. full-1 are whole tiles (tile numbers
-// 0 .. full-1); items full .. full+halves-1 are the two K halves of tiles full ..: half 0
-// runs stages [0, s_half), half 1 stages [s_half, S).  Each half writes its FP32 sums,
-// row-major 256 x 256, to part[(2 (t - full) + half) * kPartFloats ..] through the
-// epilogue's own store path; a second launch adds the two halves of each split tile and
-// runs the epilogue on the total (k_gemm_ex_fix_ew, or this kernel with fix = 1 when MX
-// codes are written).  No split: full = tiles, halves = 0.
+// K split.  Items 0 .. full-1 are whole tiles (tile numbers 0 .. full-1); items full ..
+// full+items-1 are the ks K ranges of tiles full ..: range r runs stages [r s_per,
+// (r+1) s_per), the last range up to S.  Each range writes its FP32 sums, row-major
+// 256 x 256, to part[(ks (t - full) + r) * kPartFloats ..] through the epilogue's own
+// store path; a second launch adds the ranges of each split tile in range order and runs
+// the epilogue on the total (k_gemm_ex_fix_ew, or this kernel with fix = 1 when MX codes
+// are written).  No split: full = tiles, items = 0.
 struct ExSplit {
-  int full, halves, s_half;
+  int full, items, ks, s_per;
   int fix;          // 1: the fix-up launch (one 64-thread workgroup per wave of a split tile)
   float* part;
 };
@@ -103,22 +103,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
   // work item -> tile and K-stage range [s0, s0 + S); the fix-up launch takes tile
   // full + blockIdx.x and no stages
   const int S_all = (K + 63) / 64;          // stages of the whole K
-  int t, half = -1;
+  int t, rng = -1;                          // rng: the item's K range, -1 for a whole tile
   if (sp.fix) {
     t = sp.full + (int)(blockIdx.x >> 2);
   } else if ((int)blockIdx.x < sp.full) {
     t = xcd_order(blockIdx.x, sp.full);
   } else {
-    const int k = xcd_order(blockIdx.x - sp.full, sp.halves);
-    t = sp.full + (k >> 1);
-    half = k & 1;
+    const int k = xcd_order(blockIdx.x - sp.full, sp.items);
+    t = sp.full + k / sp.ks;
+    rng = k - (t - sp.full) * sp.ks;
   }
   int tm, tn;
   tile_at(t, tiles_m, tiles_n, tm, tn);
-  const int s0 = half == 1 ? sp.s_half : 0;
-  const int S = sp.fix ? 0 : (half == 0 ? sp.s_half : S_all - s0);   // stages of this item
-  const int P0 = s0 >> 1;                   // its first scale word (s_half is even)
-  const bool last_range = half != 0;        // holds the last stage
+  const int s0 = rng > 0 ? rng * sp.s_per : 0;
+  const bool last_range = rng < 0 || rng == sp.ks - 1;   // holds the last stage
+  const int S = sp.fix ? 0 : (last_range ? S_all - s0 : sp.s_per);   // stages of this item
+  const int P0 = s0 >> 1;                   // its first scale word (s_per is even)
   const int m0 = tm * BM, n0 = tn * BNT;
   const int lane = threadIdx.x & 63;
   // the fix-up launch runs one wave per workgroup (4 per tile): its wave index comes from
@@ -431,10 +431,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     lds_barrier();
   }
   if (BNT == 256 && sp.fix) {
-    // the two K halves of the tile, row-major 256 x 256 FP32 in the workspace: their sums
-    // added (the order of two addends does not change an FP32 sum)
-    const float* p0 = sp.part + (int64_t)(2 * (t - sp.full)) * kPartFloats;
-    const float* p1 = p0 + kPartFloats;
+    // the K ranges of the tile, each row-major 256 x 256 FP32 in the workspace: their sums
+    // added in range order, as k_gemm_ex_fix_ew adds them
+    const float* p0 = sp.part + (int64_t)sp.ks * (t - sp.full) * kPartFloats;
 #pragma unroll
     for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
@@ -443,20 +442,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
         for (int q = 0; q < 4; ++q) {
           typedef float v4f __attribute__((ext_vector_type(4)));
           const int off = (128 * wm + 32 * fi + li) * 256 + 128 * wn + 32 * fj + 8 * q + 4 * lg;
-          const v4f a = *reinterpret_cast<const v4f*>(p0 + off), b = *reinterpret_cast<const v4f*>(p1 + off);
+          v4f a = *reinterpret_cast<const v4f*>(p0 + off);
+          for (int r = 1; r < sp.ks; ++r) a += *reinterpret_cast<const v4f*>(p0 + (int64_t)r * kPartFloats + off);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[fi][fj][4 * q + e] = a[e] + b[e];
+          for (int e = 0; e < 4; ++e) acc[fi][fj][4 * q + e] = a[e];
         }
   }
-  // a K half writes its FP32 sums through the epilogue's own store path: alpha 1 (exact),
+  // a K range writes its FP32 sums through the epilogue's own store path: alpha 1 (exact),
   // no bias, activation or codes, fp32 rows of 256 into its slot of the workspace
   GemmEpilogue epx = ep;
   int Mx = M, Nx = N, m0x = m0, n0x = n0;
-  if (BNT == 256 && half >= 0) {
+  if (BNT == 256 && rng >= 0) {
     epx.alpha = 1.0f;
     epx.bias = nullptr;
     epx.act = 0;
-    epx.y = sp.part + (int64_t)(2 * (t - sp.full) + half) * kPartFloats;
+    epx.y = sp.part + ((int64_t)sp.ks * (t - sp.full) + rng) * kPartFloats;
     epx.y_bf16 = 0;
     epx.ld_y = 256;
     epx.y_vec16 = 1;
@@ -611,8 +611,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
 
 // Fix-up of the split tiles when no MX codes are written: elementwise over the tiles'
 // 256 x 256 outputs, 4 consecutive columns per thread, 64 workgroups per tile.
-// v = act(alpha * (h0 + h1) + bias[col]), rounded and stored as the epilogue of
-// k_gemm_ex does it (the same FP32 operations in the same order, so the same bits).
+// v = act(alpha * (((h0 + h1) + h2) + ...) + bias[col]) over the tile's K ranges, rounded
+// and stored as the epilogue of k_gemm_ex does it (the same FP32 operations in the same
+// order, so the same bits).
 __global__ __launch_bounds__(256) void k_gemm_ex_fix_ew(int M, int N, int tiles_m, int tiles_n, const GemmEpilogue ep,
                                                        const ExSplit sp) {
   const int j = (int)(blockIdx.x >> 6);                 // split tile
@@ -623,14 +624,15 @@ __global__ __launch_bounds__(256) void k_gemm_ex_fix_ew(int M, int N, int tiles_
   const int row = tm * BM + r, col0 = tn * BN + c;
   if (row >= M || col0 >= N) return;
   typedef float v4f __attribute__((ext_vector_type(4)));
-  const float* p0 = sp.part + (int64_t)(2 * j) * kPartFloats + e0;
-  const v4f a = *reinterpret_cast<const v4f*>(p0), b = *reinterpret_cast<const v4f*>(p0 + kPartFloats);
+  const float* p0 = sp.part + (int64_t)sp.ks * j * kPartFloats + e0;
+  v4f a = *reinterpret_cast<const v4f*>(p0);
+  for (int k = 1; k < sp.ks; ++k) a += *reinterpret_cast<const v4f*>(p0 + (int64_t)k * kPartFloats);
   const bool has_bias = ep.bias != nullptr;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int col = col0 + e;
     if (col >= N) break;
-    const float acc = a[e] + b[e];
+    const float acc = a[e];
     float v = has_bias ? __builtin_fmaf(ep.alpha, acc, ep.bias[col]) : ep.alpha * acc;
     if (ep.act) v = silu(v);
     if (ep.y_bf16)
@@ -640,22 +642,44 @@ __global__ __launch_bounds__(256) void k_gemm_ex_fix_ew(int M, int N, int tiles_
   }
 }
 
-// K split of the last round: with P workgroups resident at once (one per CU) and T tiles,
-// the last round holds R = T mod P tiles.  When there is more than one round and
-// R <= P / 2, those tiles run as 2R K halves (of at least 4 stages each), so the last
-// round takes half a tile's time instead of a whole one.
+// K split, with P workgroups resident at once (one per CU) and T tiles of S stages.
+// Last round: when there is more than one round and the last holds R = T mod P <= P / 2
+// tiles, those tiles run as 2R K halves, so the last round takes half a tile's time
+// instead of a whole one.  Under-filled grid: when T <= P / 2, every tile runs as ks K
+// ranges of s_per stages (the last one the rest, at most s_per), s_per even (whole scale
+// words) and ks <= min(P / T, 16), so that up to P workgroups share the work, if that
+// shortens the longest item by more than the split costs: about 16 stage times for the
+// per-call workspace, the fix-up launch and the wider partial stores, plus the read of the
+// partial sums, one stage time per 16 ranges.  Measured, whole against split: 256 x 256 x
+// 512 20 against 34 us (kept whole), x 1000 29 against 28 (kept whole), x 2048 45
+// against 38; 1024 x 1024 x 4096 79 against 48; 2048 x 2048 x 8192 151 against 88.  At
+// most P ranges in all, so the workspace stays within P tiles of FP32.
+constexpr int kMaxRanges = 16;
+
 ExSplit plan_split(int64_t tiles, int64_t K, int cus) {
   ExSplit sp;
   sp.full = (int)tiles;
-  sp.halves = 0;
-  sp.s_half = 0;
+  sp.items = 0;
+  sp.ks = 1;
+  sp.s_per = 0;
   sp.fix = 0;
   sp.part = nullptr;
   const int64_t S = (K + 63) / 64, R = cus > 0 ? tiles % cus : 0;
   if (tiles > cus && R > 0 && 2 * R <= cus && S >= 8) {
     sp.full = (int)(tiles - R);
-    sp.halves = (int)(2 * R);
-    sp.s_half = (int)(2 * (S / 4));          // even: a whole number of scale words
+    sp.ks = 2;
+    sp.items = (int)(2 * R);
+    sp.s_per = (int)(2 * (S / 4));           // even: a whole number of scale words
+  } else if (cus > 0 && tiles >= 1 && 2 * tiles <= cus && S >= 8) {
+    const int64_t ks_max = cus / tiles < kMaxRanges ? cus / tiles : kMaxRanges;
+    const int64_t s_per = 2 * ((S + 2 * ks_max - 1) / (2 * ks_max));
+    const int64_t ks = (S + s_per - 1) / s_per;
+    if (ks >= 2 && S - s_per >= 16 + ks * tiles / 16) {
+      sp.full = 0;
+      sp.ks = (int)ks;
+      sp.items = (int)(ks * tiles);
+      sp.s_per = (int)s_per;
+    }
   }
   return sp;
 }
@@ -672,6 +696,12 @@ ExSplit plan_split(int64_t tiles, int64_t K, int cus) {
 // width.
 constexpr double kRoundFixed = 8.5, kNarrowCost = 0.83, kSplitFixed = 5.0, kFixupPerTile = 0.1;
 
+// MXQ_EXACT_KSPLIT=0 in the environment turns the K split off (every tile whole).
+bool ksplit_enabled() {
+  const char* e = getenv("MXQ_EXACT_KSPLIT");
+  return !(e != nullptr && strcmp(e, "0") == 0);
+}
+
 int choose_tile_n(int64_t M, int64_t N, int64_t K, int cus) {
   if (const char* e = getenv("MXQ_EXACT_TILE_N")) {
     if (strcmp(e, "192") == 0) return 192;
@@ -681,9 +711,9 @@ int choose_tile_n(int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t T256 = tm * ((N + 255) / 256), T192 = tm * ((N + 191) / 192);
   if (T256 <= P) return 256;
   const double round = (double)S + kRoundFixed;
-  const ExSplit sp = plan_split(T256, K, cus);
-  const double wide = sp.halves > 0 ? (double)(sp.full / P) * round + (double)(S / 2) + kRoundFixed + kSplitFixed +
-                                          kFixupPerTile * (double)(sp.halves / 2)
+  const ExSplit sp = plan_split(T256, K, ksplit_enabled() ? cus : 0);
+  const double wide = sp.items > 0 ? (double)(sp.full / P) * round + (double)(S / 2) + kRoundFixed + kSplitFixed +
+                                         kFixupPerTile * (double)(sp.items / 2)
                                     : (double)((T256 + P - 1) / P) * round;
   const double narrow = (double)((T192 + P - 1) / P) * kNarrowCost * round;
   return narrow < wide ? 192 : 256;
@@ -703,13 +733,14 @@ hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t 
     attr_set[dev] = true;
   }
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BNT - 1) / BNT);
-  hipLaunchKernelGGL(kern, dim3(sp.full + sp.halves), dim3(kThreads), kLdsBytes, stream, (int)M, (int)N, (int)K,
+  hipLaunchKernelGGL(kern, dim3(sp.full + sp.items), dim3(kThreads), kLdsBytes, stream, (int)M, (int)N, (int)K,
                      tiles_m, tiles_n, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, sp);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || sp.halves == 0) return e;
+  if (e != hipSuccess || sp.items == 0) return e;
+  const int split_tiles = sp.items / sp.ks;
   if (!ep.qc) {
     // plain outputs: the elementwise fix-up (64 workgroups per split tile)
-    hipLaunchKernelGGL(k_gemm_ex_fix_ew, dim3(32 * sp.halves), dim3(256), 0, stream, (int)M, (int)N, tiles_m, tiles_n,
+    hipLaunchKernelGGL(k_gemm_ex_fix_ew, dim3(64 * split_tiles), dim3(256), 0, stream, (int)M, (int)N, tiles_m, tiles_n,
                        ep, sp);
     return hipGetLastError();
   }
@@ -718,7 +749,7 @@ hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t 
   // the CUs idle)
   ExSplit fx = sp;
   fx.fix = 1;
-  hipLaunchKernelGGL(kern, dim3(2 * sp.halves), dim3(64), kEpiWaveBytes, stream, (int)M, (int)N, (int)K, tiles_m,
+  hipLaunchKernelGGL(kern, dim3(4 * split_tiles), dim3(64), kEpiWaveBytes, stream, (int)M, (int)N, (int)K, tiles_m,
                      tiles_n, xc, ld_x, xs, ld_xs, wc, ld_w, ws, ld_ws, ep, fx);
   return hipGetLastError();
 }
@@ -734,7 +765,7 @@ hipError_t launch_w(int bn, int64_t M, int64_t N, int64_t K, const uint8_t* xc, 
 // The split plan of the chosen width: the K split exists for full-width tiles only.
 ExSplit plan_for(int bn, int64_t M, int64_t N, int64_t K, int cus) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + bn - 1) / bn);
-  return plan_split(tiles, K, bn == 256 ? cus : 0);
+  return plan_split(tiles, K, bn == 256 && ksplit_enabled() ? cus : 0);
 }
 
 }  // namespace ex
@@ -743,7 +774,7 @@ ExSplit plan_for(int bn, int64_t M, int64_t N, int64_t K, int cus) {
 int64_t gemm_exact_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   const int cus = device_cu_count();
   const ex::ExSplit sp = ex::plan_for(ex::choose_tile_n(M, N, K, cus), M, N, K, cus);
-  return (int64_t)sp.halves * ex::kPartFloats * (int64_t)sizeof(float);
+  return (int64_t)sp.items * ex::kPartFloats * (int64_t)sizeof(float);
 }
 
 hipError_t launch_gemm_exact(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
@@ -753,8 +784,8 @@ hipError_t launch_gemm_exact(int64_t M, int64_t N, int64_t K, const uint8_t* xc,
   const int cus = device_cu_count();
   const int bn = ex::choose_tile_n(M, N, K, cus);
   ex::ExSplit sp = ex::plan_for(bn, M, N, K, cus);
-  if (sp.halves > 0) {
-    if (workspace == nullptr || workspace_bytes < (int64_t)sp.halves * ex::kPartFloats * (int64_t)sizeof(float))
+  if (sp.items > 0) {
+    if (workspace == nullptr || workspace_bytes < (int64_t)sp.items * ex::kPartFloats * (int64_t)sizeof(float))
       sp = ex::plan_for(bn, M, N, K, 0);      // no room: the whole tiles only
     else
       sp.part = static_cast<float*>(workspace);

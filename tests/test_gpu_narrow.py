@@ -1,12 +1,12 @@
 """GPU parity of the exact-product GEMM's 256 x 192 tile (the width the library picks where
 it fills the tile rounds better, e.g. 4096 x 6144 on 256 CUs).
 
-MXQ_EXACT_TILE_N forces a width.  The two widths run the same MFMAs over the same k16 steps
-for every output element, so their outputs must be identical bit for bit; the narrow tile
-is also checked against the FP64 oracle within 1e-5 * sum_k |s x w| (every element of a
-ragged problem, a sample of the full-size ragged workload), with bias, alpha, SiLU, bf16
-and fp32 outputs, mixed E5M2 x E4M3 operands, and the producer-fused MX output byte for
-byte against quantize of the bf16 Y."""
+MXQ_EXACT_TILE_N forces a width (MXQ_EXACT_KSPLIT=0 keeps every tile whole).  The two
+widths run the same MFMAs over the same k16 steps for every output element, so whole tiles
+must give identical bits; the narrow tile is also checked against the FP64 oracle within
+1e-5 * sum_k |s x w| (every element of a ragged problem, a sample of the full-size ragged
+workload), with bias, alpha, SiLU, bf16 and fp32 outputs, mixed E5M2 x E4M3 operands, and
+the producer-fused MX output byte for byte against quantize of the bf16 Y."""
 import numpy as np
 import pytest
 import torch
@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 ENV = "MXQ_EXACT_TILE_N"
+KSPLIT = "MXQ_EXACT_KSPLIT"
 
 
 def operands(M, N, K, seed, fx="e4m3", fw="e4m3", xstd=1.0):
@@ -32,11 +33,15 @@ def operands(M, N, K, seed, fx="e4m3", fw="e4m3", xstd=1.0):
 
 
 def both_widths(monkeypatch, *args, **kw):
+    """The call with each width forced and the K split off (a split changes the rounding
+    order of the FP32 sums, so only whole tiles compare bit for bit)."""
     out = {}
+    monkeypatch.setenv(KSPLIT, "0")
     for width in ("192", "256"):
         monkeypatch.setenv(ENV, width)
         out[width] = mxq.gemm(*args, **kw)
     monkeypatch.delenv(ENV)
+    monkeypatch.delenv(KSPLIT)
     torch.cuda.synchronize()
     return out["192"], out["256"]
 
@@ -106,6 +111,7 @@ def test_narrow_fused_codes(monkeypatch):
     monkeypatch.setenv(ENV, "192")
     y, qc, qs = mxq.gemm(xc, xs, wc, ws, K, bias=b, out_dtype=torch.bfloat16, act="silu", quant_out="e4m3")
     monkeypatch.setenv(ENV, "256")
+    monkeypatch.setenv(KSPLIT, "0")
     y2, qc2, qs2 = mxq.gemm(xc, xs, wc, ws, K, bias=b, out_dtype=torch.bfloat16, act="silu", quant_out="e4m3")
     torch.cuda.synchronize()
     rc, rs = oracle.quantize(host_src(y.cpu()), "e4m3")

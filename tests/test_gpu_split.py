@@ -1,8 +1,10 @@
-"""GPU parity of the exact-product GEMM when the last round of tiles runs as K halves (more
-tiles than CUs, and a last round at most half full): every element of the split tiles and
-a sample of the rest against the FP64 oracle within 1e-5 * sum_k |s x w|, with ragged M, N
-and K, a bias, alpha, bf16 and fp32 outputs and the SiLU epilogue; the producer-fused MX
-output of split tiles byte for byte against quantize of the bf16 Y; and determinism."""
+"""GPU parity of the exact-product GEMM when tiles run as K ranges: the last round of tiles
+as K halves (more tiles than CUs, a last round at most half full), and every tile of an
+under-filled grid (at most half as many tiles as CUs) as up to 16 ranges.  Every element of
+split tiles and a sample of the rest against the FP64 oracle within 1e-5 * sum_k |s x w|,
+with ragged M, N and K, a bias, alpha, bf16 and fp32 outputs and the SiLU epilogue; the
+producer-fused MX output of split tiles byte for byte against quantize of the bf16 Y; and
+determinism."""
 import numpy as np
 import pytest
 import torch
@@ -131,3 +133,71 @@ def test_split_deterministic():
     y0 = mxq.gemm(xc, xs, wc, ws, K, out_dtype=torch.float32, accum="fp32")
     for _ in range(2):
         assert torch.equal(y0, mxq.gemm(xc, xs, wc, ws, K, out_dtype=torch.float32, accum="fp32"))
+
+
+# ---- under-filled grids: every tile as ks K ranges (at most P / 2 tiles)
+
+def ranges(M, N, K):
+    """(ks, s_per) as the library plans an under-filled grid of 256 x 256 tiles, or None."""
+    P = cus()
+    T = ((M + TILE - 1) // TILE) * ((N + TILE - 1) // TILE)
+    S = (K + 63) // 64
+    if T < 1 or 2 * T > P or S < 8:
+        return None
+    ks_max = min(P // T, 16)
+    s_per = 2 * ((S + 2 * ks_max - 1) // (2 * ks_max))
+    ks = (S + s_per - 1) // s_per
+    return (ks, s_per) if ks >= 2 and S - s_per >= 16 + ks * T // 16 else None
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 2048), (200, 130, 4001), (256, 256, 1536)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_ranges_one_tile_every_element(M, N, K, out):
+    """One tile split into K ranges (16 of 2 stages; 16 of 4 stages with the last one 3
+    stages and a partial final block; 12 of 2 stages): every element within the strict
+    bound, with bias and alpha."""
+    assert ranges(M, N, K) is not None
+    say("K ranges, one tile %dx%dx%d %s: %s" % (M, N, K, out, ranges(M, N, K)))
+    xc, xs, wc, ws, b = operands(M, N, K, 35)
+    y = mxq.gemm(xc, xs, wc, ws, K, alpha=-1.25, bias=b, out_dtype=out, accum="fp32")
+    torch.cuda.synchronize()
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    check_at(xc, xs, wc, ws, K, y, ii.ravel(), jj.ravel(), out, alpha=-1.25, bias=b, what="K ranges one tile")
+
+
+def test_ranges_sixteen_tiles_sampled():
+    """16 tiles of a skinny problem with long K (1024 x 1024 x 4096: 16 ranges of 4 stages
+    per tile, 256 items): a sample, whole rows at tile edges and a whole column."""
+    M, N, K = 1024, 1024, 4096
+    assert ranges(M, N, K) == (16, 4)
+    xc, xs, wc, ws, b = operands(M, N, K, 36)
+    y = mxq.gemm(xc, xs, wc, ws, K, bias=b, out_dtype=torch.float32, accum="fp32")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    rows = np.array([0, 255, 256, 1023])
+    ii = np.concatenate([rng.integers(0, M, 5000), np.repeat(rows, N), np.arange(M)])
+    jj = np.concatenate([rng.integers(0, N, 5000), np.tile(np.arange(N), rows.size), np.full(M, 511)])
+    check_at(xc, xs, wc, ws, K, y, ii, jj, torch.float32, bias=b, what="K ranges 16 tiles")
+
+
+def test_ranges_fused_codes_and_determinism():
+    """The producer-fused MX output of a split tile (the fix-up runs the kernel's own
+    epilogue): codes and scales equal quantize of the bf16 Y of the same call; repeated
+    calls give identical bytes."""
+    M, N, K = 256, 256, 1536
+    assert ranges(M, N, K) is not None
+    xc, xs, wc, ws, b = operands(M, N, K, 37, xstd=8.0)
+    y, qc, qs = mxq.gemm(xc, xs, wc, ws, K, bias=b, out_dtype=torch.bfloat16, accum="fp32", act="silu",
+                         quant_out="e4m3")
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize(host_src(y.cpu()), "e4m3")
+    assert np.array_equal(qc.cpu().numpy()[:, :N], rc)
+    assert np.array_equal(qs.cpu().numpy(), rs)
+    v = mxq.gemm(xc, xs, wc, ws, K, bias=b, out_dtype=torch.float32, accum="fp32")
+    ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    check_at(xc, xs, wc, ws, K, v, ii.ravel(), jj.ravel(), torch.float32, bias=b, what="K ranges pre-activation")
+    for _ in range(2):
+        y2, qc2, qs2 = mxq.gemm(xc, xs, wc, ws, K, bias=b, out_dtype=torch.bfloat16, accum="fp32", act="silu",
+                                quant_out="e4m3")
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)) and torch.equal(qc, qc2) and torch.equal(qs, qs2)
+        assert torch.equal(v, mxq.gemm(xc, xs, wc, ws, K, bias=b, out_dtype=torch.float32, accum="fp32"))
