@@ -431,9 +431,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
     lds_barrier();
   }
   if (BNT == 256 && sp.fix) {
-    // the K ranges of the tile, each row-major 256 x 256 FP32 in the workspace: their sums
-    // added in range order, as k_gemm_ex_fix_ew adds them
+    // the tile's first two range slots of the workspace, row-major 256 x 256 FP32, added:
+    // ranges 0 and 1, or with more ranges the sum of all but the last and the last one
+    // (k_gemm_ex_sum_ranges put them there), so the total is added in range order
     const float* p0 = sp.part + (int64_t)sp.ks * (t - sp.full) * kPartFloats;
+    const float* p1 = p0 + kPartFloats;
 #pragma unroll
     for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
@@ -442,10 +444,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_ex(int M, int N, int K, in
         for (int q = 0; q < 4; ++q) {
           typedef float v4f __attribute__((ext_vector_type(4)));
           const int off = (128 * wm + 32 * fi + li) * 256 + 128 * wn + 32 * fj + 8 * q + 4 * lg;
-          v4f a = *reinterpret_cast<const v4f*>(p0 + off);
-          for (int r = 1; r < sp.ks; ++r) a += *reinterpret_cast<const v4f*>(p0 + (int64_t)r * kPartFloats + off);
+          const v4f a = *reinterpret_cast<const v4f*>(p0 + off), b = *reinterpret_cast<const v4f*>(p1 + off);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[fi][fj][4 * q + e] = a[e];
+          for (int e = 0; e < 4; ++e) acc[fi][fj][4 * q + e] = a[e] + b[e];
         }
   }
   // a K range writes its FP32 sums through the epilogue's own store path: alpha 1 (exact),
@@ -642,6 +643,24 @@ __global__ __launch_bounds__(256) void k_gemm_ex_fix_ew(int M, int N, int tiles_
   }
 }
 
+// Before the fix-up through the kernel's own epilogue (MX codes written) of tiles split
+// into more than two K ranges: ranges 0 .. ks-2 added in range order into the tile's
+// first slot and the last range copied into the second, so that the kernel's sum of the
+// two slots is the fix-up's ((h0 + h1) + ...) + h_{ks-1} (a fix path that reads one slot
+// made the register allocator spill twice as many values in the main kernel).  4
+// consecutive values per thread, 64 workgroups per tile.
+__global__ __launch_bounds__(256) void k_gemm_ex_sum_ranges(const ExSplit sp) {
+  const int j = (int)(blockIdx.x >> 6);                 // split tile
+  const int e0 = (int)((blockIdx.x & 63) * 1024 + 4 * threadIdx.x);
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  float* p0 = sp.part + (int64_t)sp.ks * j * kPartFloats + e0;
+  v4f a = *reinterpret_cast<const v4f*>(p0);
+  for (int k = 1; k < sp.ks - 1; ++k) a += *reinterpret_cast<const v4f*>(p0 + (int64_t)k * kPartFloats);
+  const v4f last = *reinterpret_cast<const v4f*>(p0 + (int64_t)(sp.ks - 1) * kPartFloats);
+  *reinterpret_cast<v4f*>(p0) = a;
+  *reinterpret_cast<v4f*>(p0 + kPartFloats) = last;
+}
+
 // K split, with P workgroups resident at once (one per CU) and T tiles of S stages.
 // Last round: when there is more than one round and the last holds R = T mod P <= P / 2
 // tiles, those tiles run as 2R K halves, so the last round takes half a tile's time
@@ -747,6 +766,11 @@ hipError_t launch_f(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t 
   // with MX codes: the kernel's own epilogue, one wave per workgroup, four per split tile,
   // 32 KiB of LDS each, so every CU takes part (one 4-wave workgroup per tile left half
   // the CUs idle)
+  if (sp.ks > 2) {
+    hipLaunchKernelGGL(k_gemm_ex_sum_ranges, dim3(64 * split_tiles), dim3(256), 0, stream, sp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   ExSplit fx = sp;
   fx.fix = 1;
   hipLaunchKernelGGL(kern, dim3(4 * split_tiles), dim3(64), kEpiWaveBytes, stream, (int)M, (int)N, (int)K, tiles_m,
