@@ -1,8 +1,8 @@
 """mxq_gemm_ex_noalloc (the allocation-free entry point, whose K-split workspace is a static
 device array) against mxq_gemm_ex on the same operands: identical bytes, on two calls in a
 row, the second with a smaller input (so the second call runs on scratch that still holds
-the first call's sums), both shapes with more tiles than CUs so that the last round is
-split along K and the scratch is used."""
+the first call's sums); once with more tiles than CUs (the last round split into K
+halves), once with an under-filled grid (every tile split into K ranges)."""
 import ctypes
 
 import numpy as np
@@ -50,6 +50,23 @@ def test_noalloc_matches_gemm_ex_on_two_calls():
     for i, (M, N, K) in enumerate(shapes):
         say("no-alloc gemm call %d: %dx%dx%d" % (i, M, N, K))
         xc, xs, wc, ws, b = operands(M, N, K, 40 + i)
+        y_ref = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        y_na = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        run(mxq.mxq_gemm_ex, xc, xs, wc, ws, b, K, y_ref)
+        run(mxq.mxq_gemm_ex_noalloc, xc, xs, wc, ws, b, K, y_na)
+        torch.cuda.synchronize()
+        assert not torch.isnan(y_ref).any()
+        assert torch.equal(y_ref.view(torch.int32), y_na.view(torch.int32)), "call %d differs" % i
+
+
+def test_noalloc_matches_gemm_ex_k_ranges():
+    """Under-filled grids split every tile into K ranges: 16 tiles x 16 ranges fill the
+    whole static scratch (64 MiB), then a one-tile problem of 16 ranges runs on scratch
+    that still holds the first call's sums; identical bytes to mxq_gemm_ex both times."""
+    shapes = [(1024, 1024, 4096), (256, 256, 2048)]
+    for i, (M, N, K) in enumerate(shapes):
+        say("no-alloc gemm, K ranges, call %d: %dx%dx%d" % (i, M, N, K))
+        xc, xs, wc, ws, b = operands(M, N, K, 50 + i)
         y_ref = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
         y_na = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
         run(mxq.mxq_gemm_ex, xc, xs, wc, ws, b, K, y_ref)
