@@ -329,7 +329,8 @@ int mxq_gemm_ex(int64_t M, int64_t N, int64_t K,
  * loops, harnesses that forbid allocation.
  *
  * Arguments, results and errors as for mxq_gemm_ex, bit for bit.  The K split's workspace
- * is a file-scope device array of 64 MiB (enough for a device of up to 256 CUs) that
+ * (256 KiB per K range, at most one range per CU) is a file-scope device array of 64 MiB
+ * (enough for a device of up to 256 CUs) that
  * every device the library runs on holds from load until the process ends; a problem
  * that would need more returns MXQ_ERR_SCRATCH.  All calls on one device share that
  * array: calls that may overlap on one device (different streams, no ordering between
