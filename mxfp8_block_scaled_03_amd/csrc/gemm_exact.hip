@@ -17,11 +17,12 @@
 //
 // Work split.  256x256 output tile per workgroup of 4 waves, one wave per SIMD; wave
 // (wm, wn) owns the 128x128 block of X rows 128 wm.. and W rows 128 wn.. (4x4 MFMA tiles,
-// 256 FP32 accumulators per lane).  A narrow variant (256x192 tile, 128x96 per wave, 4x3
-// MFMA tiles) runs the same loop without the fourth W fragment column; it is chosen on the
-// host where its rounds fill the CUs better.  A wave decodes each of its 256 fragment rows once per
+// 256 FP32 accumulators per lane).  A wave decodes each of its 256 fragment rows once per
 // K element: two conversion instructions per MFMA, which the matrix core's 32-cycle issue
-// interval hides.
+// interval hides.  A narrow variant (256x192 tile, 128x96 per wave, 4x3 MFMA tiles, 7/3
+// conversions per MFMA) runs the same loop without the fourth W fragment column; the host
+// picks it where its rounds fill the CUs better.  Full-width tiles may also run as several
+// K ranges whose sums a fix-up adds (ExSplit below).
 //
 // K loop.  A stage is 64 bytes of K (two 32-element blocks) of 256 X rows and 256 W rows,
 // 32 KiB in LDS, 16-byte chunk c of row r at chunk c ^ ((r >> 2) & 3) (conflict-free
