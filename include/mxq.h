@@ -23,8 +23,8 @@
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library never
  *     synchronizes; work is enqueued on `stream` (a hipStream_t passed as void*; NULL
  *     means the default stream) and runs asynchronously.  Nothing is allocated, except
- *     the workspace of mxq_gemm / mxq_gemm_ex in the MXQ_ACC_FP32 mode when it splits the
- *     last round of tiles along K (see mxq_gemm_ex), which is taken from and given back
+ *     the workspace of mxq_gemm / mxq_gemm_ex in the MXQ_ACC_FP32 mode when it splits
+ *     tiles along K (see mxq_gemm_ex), which is taken from and given back
  *     to the device's stream-ordered memory pool on `stream` (hipMallocAsync /
  *     hipFreeAsync); mxq_gemm_ex_noalloc allocates nothing.
  *   - Sizes and leading dimensions are in ELEMENTS of the pointed-to type (bytes for
