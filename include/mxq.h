@@ -344,6 +344,23 @@ int mxq_gemm_ex_noalloc(int64_t M, int64_t N, int64_t K,
                         int q_elem, uint8_t* q_codes, int64_t ld_q_codes, uint8_t* q_scales, int64_t ld_q_scales,
                         int accum, void* stream);
 
+/*
+ * mxq_gemm_exact_plan -- how mxq_gemm / mxq_gemm_ex in the MXQ_ACC_FP32 mode with 4-byte
+ * aligned scale rows would run an M x N x K problem on a device of `cus` compute units
+ * (host logic only: no device is touched, so it also answers for other CU counts), under
+ * the environment overrides described at mxq_gemm_ex.  For tuning and tests; launches
+ * nothing.
+ *
+ * Outputs (host pointers, all required): tile_n -- the tile width, 256 or 192 (tiles are
+ * 256 rows tall); ranges_per_tile -- K ranges per split tile (1 when nothing is split);
+ * split_tiles -- tiles computed as K ranges; whole_tiles -- tiles computed whole;
+ * workspace_bytes -- the workspace the split needs (256 KiB per K range).
+ * Returns MXQ_OK, MXQ_ERR_NULL, MXQ_ERR_SHAPE (M or N < 1, K < 0, or a size >= 2^31) or
+ * MXQ_ERR_ARG (cus < 1).
+ */
+int mxq_gemm_exact_plan(int64_t M, int64_t N, int64_t K, int cus, int* tile_n, int* ranges_per_tile,
+                        int* split_tiles, int* whole_tiles, int64_t* workspace_bytes);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* mxq_status_string(int status);
 

@@ -16,6 +16,6 @@ from ._binding import (  # noqa: F401
     MXQ_ACC_FP32, MXQ_ACC_FP8_MFMA, MXQ_ACT_NONE, MXQ_ACT_SILU, MXQ_BF16, MXQ_COLWISE, MXQ_E4M3, MXQ_E5M2,
     MXQ_F32, MXQ_ROWWISE, MXQ_SCALE_CEIL, MXQ_SCALE_OCP, MxqError, dequantize, gemm, lib, library_path,
     mxq_dequantize, mxq_gemm, mxq_gemm_ex, mxq_gemm_ex_noalloc, mxq_quantize, mxq_quantize_dual, mxq_quantize_rule, mxq_quantize_scaled,
-    mxq_quantize_sr, mxq_status_string, mxq_version,
+    mxq_gemm_exact_plan, mxq_quantize_sr, mxq_status_string, mxq_version,
     quantize, quantize_dual, quantize_scaled, quantize_sr,
 )

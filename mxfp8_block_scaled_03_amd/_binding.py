@@ -68,6 +68,9 @@ def lib():
         L.mxq_status_string.argtypes = [ci]
         L.mxq_version.restype = ci
         L.mxq_version.argtypes = []
+        L.mxq_gemm_exact_plan.restype = ci
+        ip = ctypes.POINTER(ci)
+        L.mxq_gemm_exact_plan.argtypes = [i64, i64, i64, ci, ip, ip, ip, ip, ctypes.POINTER(i64)]
         _lib = L
     return _lib
 
@@ -136,6 +139,18 @@ def mxq_status_string(status: int) -> str:
 
 def mxq_version() -> int:
     return lib().mxq_version()
+
+
+def mxq_gemm_exact_plan(M: int, N: int, K: int, cus: int) -> dict:
+    """The exact-product GEMM's plan for an M x N x K problem on `cus` CUs (host logic, no
+    device): tile width, K ranges per split tile, split and whole tiles, workspace bytes.
+    Raises MxqError (a ValueError) on a negative status."""
+    c = ctypes.c_int
+    tn, ks, sp, wh, wb = c(), c(), c(), c(), ctypes.c_int64()
+    _check(lib().mxq_gemm_exact_plan(M, N, K, cus, ctypes.byref(tn), ctypes.byref(ks), ctypes.byref(sp),
+                                     ctypes.byref(wh), ctypes.byref(wb)), "mxq_gemm_exact_plan")
+    return {"tile_n": tn.value, "ranges_per_tile": ks.value, "split_tiles": sp.value, "whole_tiles": wh.value,
+            "workspace_bytes": wb.value}
 
 
 # ----------------------------------------------------------------- torch conveniences

@@ -48,6 +48,15 @@ const char* mxq_status_string(int status) {
 
 int mxq_version(void) { return 102; }
 
+int mxq_gemm_exact_plan(int64_t M, int64_t N, int64_t K, int cus, int* tile_n, int* ranges_per_tile,
+                        int* split_tiles, int* whole_tiles, int64_t* workspace_bytes) {
+  if (!tile_n || !ranges_per_tile || !split_tiles || !whole_tiles || !workspace_bytes) return MXQ_ERR_NULL;
+  if (M < 1 || N < 1 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return MXQ_ERR_SHAPE;
+  if (cus < 1) return MXQ_ERR_ARG;
+  mxq::gemm_exact_plan(M, N, K, cus, tile_n, ranges_per_tile, split_tiles, whole_tiles, workspace_bytes);
+  return MXQ_OK;
+}
+
 int mxq_quantize(const void* src, int src_type, int64_t rows, int64_t cols, int64_t ld_src, int axis, int elem,
                  uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales, void* stream) {
   return mxq_quantize_rule(src, src_type, rows, cols, ld_src, axis, elem, MXQ_SCALE_CEIL, codes, ld_codes, scales,

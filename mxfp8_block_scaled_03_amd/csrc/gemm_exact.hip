@@ -798,10 +798,22 @@ ExSplit plan_for(int bn, int64_t M, int64_t N, int64_t K, int cus) {
 }  // namespace ex
 }  // namespace
 
+void gemm_exact_plan(int64_t M, int64_t N, int64_t K, int cus, int* tile_n, int* ranges, int* split_tiles,
+                     int* whole_tiles, int64_t* workspace_bytes) {
+  const int bn = ex::choose_tile_n(M, N, K, cus);
+  const ex::ExSplit sp = ex::plan_for(bn, M, N, K, cus);
+  *tile_n = bn;
+  *ranges = sp.items > 0 ? sp.ks : 1;
+  *split_tiles = sp.items > 0 ? sp.items / sp.ks : 0;
+  *whole_tiles = sp.full;
+  *workspace_bytes = (int64_t)sp.items * ex::kPartFloats * (int64_t)sizeof(float);
+}
+
 int64_t gemm_exact_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const int cus = device_cu_count();
-  const ex::ExSplit sp = ex::plan_for(ex::choose_tile_n(M, N, K, cus), M, N, K, cus);
-  return (int64_t)sp.items * ex::kPartFloats * (int64_t)sizeof(float);
+  int bn, ks, split, whole;
+  int64_t bytes;
+  gemm_exact_plan(M, N, K, device_cu_count(), &bn, &ks, &split, &whole, &bytes);
+  return bytes;
 }
 
 hipError_t launch_gemm_exact(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,

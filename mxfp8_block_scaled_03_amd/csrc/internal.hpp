@@ -70,6 +70,10 @@ struct GemmEpilogue {
 // Exact-product GEMM.  workspace: device memory for the K split of the last round's tiles
 // (gemm_exact_workspace_bytes(M, N, K) bytes; with less, or none, the tiles run whole).
 int64_t gemm_exact_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// The exact GEMM's plan for `cus` CUs (host logic only): tile width, K ranges per split
+// tile, split tiles, whole tiles and workspace bytes.
+void gemm_exact_plan(int64_t M, int64_t N, int64_t K, int cus, int* tile_n, int* ranges, int* split_tiles,
+                     int* whole_tiles, int64_t* workspace_bytes);
 hipError_t launch_gemm_exact(int64_t M, int64_t N, int64_t K, const uint8_t* xc, int64_t ld_x, const uint8_t* xs,
                              int64_t ld_xs, int x_fmt, const uint8_t* wc, int64_t ld_w, const uint8_t* ws,
                              int64_t ld_ws, int w_fmt, const GemmEpilogue& ep, void* workspace,

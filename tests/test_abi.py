@@ -18,7 +18,7 @@ def declared_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert {"mxq_quantize", "mxq_quantize_rule", "mxq_quantize_dual", "mxq_quantize_sr", "mxq_quantize_scaled", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex", "mxq_gemm_ex_noalloc",
+    assert {"mxq_quantize", "mxq_quantize_rule", "mxq_quantize_dual", "mxq_quantize_sr", "mxq_quantize_scaled", "mxq_dequantize", "mxq_gemm", "mxq_gemm_ex", "mxq_gemm_ex_noalloc", "mxq_gemm_exact_plan",
             "mxq_status_string", "mxq_version"} <= set(declared_symbols())
 
 
