@@ -15,8 +15,13 @@ bound, is timed only as a labelled component.  The standalone quantize of 2^28 b
 elements is reported against the HBM peak.  The CPU oracle is timed on a bounded sample
 of the same step.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-calibration]
-                       [--headline-only] [--only KERNEL]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms T] [--no-cpu]
+                       [--copy-calibration] [--headline-only] [--only KERNEL]
+
+Before the W warmup steps the step runs untimed, in blocks of 20, for at least T ms of
+wall time (default 150; 0 skips it): the clock of a GPU that was idle rises over the first
+~40 ms of sustained load, and the timed steps should see the sustained rate.  The JSON
+line reports these steps under "settle".
 
 --headline-only times the step alone (no components, no CPU leg): the short run that
 counter passes profile.
@@ -54,6 +59,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--settle-ms", type=float, default=150.0,
+                   help="untimed steps before the warmup, for at least this much wall time (0: none)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU-oracle sample time")
     p.add_argument("--copy-calibration", action="store_true", help="also run a copy of known size (counter runs)")
@@ -83,6 +90,19 @@ KERNEL_SOURCES = {
 }
 GEMM_KERNEL_NAME = "mxq gemm, exact-product mode (ex::k_gemm_ex<0,0,256>: codes decoded to bf16 in registers, bf16 matrix cores)"
 FP8_LABEL = "FP8 matrix cores, 8-product groups truncated ~13 bits below their largest (outside 1e-5*T)"
+
+
+def settle(torch, fn, ms: float, block: int = 10) -> int:
+    """Runs fn untimed, in blocks of `block` calls, until `ms` of wall time have passed (the
+    clock of a GPU that was idle rises over the first tens of ms of sustained load); returns
+    the number of calls (0 when ms <= 0)."""
+    n, t = 0, time.perf_counter()
+    while (time.perf_counter() - t) * 1e3 < ms:
+        for _ in range(block):
+            fn()
+        torch.cuda.synchronize()
+        n += block
+    return n
 
 
 def source_digest(paths) -> str:
@@ -169,6 +189,12 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    # an idle GPU's clock rises over the first ~40 ms of sustained load (the GEMM from a
+    # cold start: 242, 228, 223, ... 211 us per call in blocks of 20 calls), so the step
+    # runs untimed for --settle-ms of wall time before the warmup steps
+    t_settle = time.perf_counter()
+    settle_steps = settle(torch, step, args.settle_ms, 20)
+    settle_ms = (time.perf_counter() - t_settle) * 1e3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -199,6 +225,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"steps": settle_steps, "ms": round(settle_ms, 1),
+                   "why": "untimed steps before the warmup until the clock of an idle GPU has risen"},
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -228,8 +256,8 @@ def main():
     gf_args = list(g_args)
     gf_args[15] = yf.data_ptr()
     gf_args[18] = mxq.MXQ_ACC_FP8_MFMA
-    for _ in range(3):
-        L.mxq_gemm(*gf_args)
+    comp_settle_ms = args.settle_ms / 2          # each component runs untimed this long first
+    settle(torch, lambda: L.mxq_gemm(*gf_args), comp_settle_ms)
     ee = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
     for a, b in ee:
         a.record(stream)
@@ -248,9 +276,8 @@ def main():
     qs = torch.empty((qx.shape[0], qx.shape[1] // 32), dtype=torch.uint8, device=dev)
     q_q = (qx.data_ptr(), mxq.MXQ_BF16, qx.shape[0], qx.shape[1], qx.stride(0), mxq.MXQ_ROWWISE, mxq.MXQ_E4M3,
            qc.data_ptr(), qc.stride(0), qs.data_ptr(), qs.stride(0), sh)
-    for _ in range(3):
-        L.mxq_quantize(*q_q)
-    torch.cuda.synchronize()
+    L.mxq_quantize(*q_q)
+    settle(torch, lambda: L.mxq_quantize(*q_q), comp_settle_ms)
     nq = 20
     qe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nq)]
     for a, b in qe:
@@ -267,6 +294,7 @@ def main():
     def time_calls(fn, n=10):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         fn()
+        settle(torch, fn, comp_settle_ms)
         a.record(stream)
         for _ in range(n):
             fn()
@@ -307,6 +335,7 @@ def main():
     # X alone: 20 launches between two events (a single launch is short enough that the
     # host could fall behind the GPU)
     xa, xb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    settle(torch, lambda: L.mxq_quantize(*q_x), comp_settle_ms)
     xa.record(stream)
     for _ in range(20):
         L.mxq_quantize(*q_x)
@@ -490,6 +519,7 @@ def only_quantize(args, torch, mxq, wl, dev):
     st = call()
     if st != 0:
         raise RuntimeError("%s failed: %s" % (args.only, mxq.mxq_status_string(st)))
+    settle(torch, call, args.settle_ms)
     for _ in range(args.warmup):
         call()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -524,6 +554,7 @@ def only_gemm(args, torch, mxq, wl, dev):
     st = L.mxq_gemm(*a)
     if st != 0:
         raise RuntimeError("%s failed: %s" % (args.only, mxq.mxq_status_string(st)))
+    settle(torch, lambda: L.mxq_gemm(*a), args.settle_ms)
     for _ in range(args.warmup):
         L.mxq_gemm(*a)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -562,6 +593,7 @@ def only_reference(args, torch, wl, dev):
         work = x.numel() * (2 + y.element_size())
         what = "[16384][16384] bf16 -> %s elementwise copy" % ("int8" if kind == "ref_cast" else "bf16")
     stream = torch.cuda.current_stream()
+    settle(torch, call, args.settle_ms)
     for _ in range(args.warmup + 1):
         call()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
