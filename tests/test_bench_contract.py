@@ -38,3 +38,22 @@ def test_traffic_is_keyed_to_the_kernel_sources(tmp_path, monkeypatch):
         assert bench.load_traffic(key) is None
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
     assert bench.load_traffic("gemm_exact") is None
+
+
+def test_settle_runs_whole_blocks_for_the_wall_time():
+    """The untimed settle phase: nothing at 0 ms, whole blocks with a synchronization after
+    each until the wall time has passed."""
+    class FakeCuda:
+        syncs = 0
+
+        @classmethod
+        def synchronize(cls):
+            cls.syncs += 1
+
+    class FakeTorch:
+        cuda = FakeCuda
+
+    calls = []
+    assert bench.settle(FakeTorch, lambda: calls.append(1), 0.0) == 0 and not calls
+    n = bench.settle(FakeTorch, lambda: calls.append(1), 5.0, block=7)
+    assert n == len(calls) and n > 0 and n % 7 == 0 and FakeCuda.syncs == n // 7
